@@ -1,0 +1,297 @@
+"""CPU oracle for the ReDrafter verification step -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct fp64 (numpy) statement of what one
+verification step computes.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.
+It shares no code with the HIP library and imports nothing from it.
+
+Sources (cited by page title and section):
+  [TRT] "ReDrafter in NVIDIA TensorRT-LLM" blog (Chinese and English copies),
+        intro; "Inflight-batching Compatible Engine"; "Implementing in-Engine
+        Validation and Drafting" (the PyTorch `unpack` listing).
+  [NEWS] Apple/NVIDIA ReDrafter news article, sections "RNN draft model" and
+        "Dynamic tree attention", and the greedy-decoding benchmark paragraph.
+  [PAPER] "Recurrent Drafter for Fast Speculative Decoding in Large Language
+        Models", abstract point (2).
+  [SURV] "Accelerating LLM inference with speculative decoding" survey,
+        section SpecInfer / "Token Tree Verifier".
+
+Readings where the pages are silent (each listed with its reason in the
+design notes): packed slots are in first-occurrence order of a beam-major
+scan; beam position 0 is the target's initial token; attention scale is
+1/sqrt(D) with every cached key visible; grouped-query heads map to KV head
+h // (Hq/Hkv); argmax ties resolve to the lowest vocabulary id and equal
+match lengths to the lowest beam index.
+
+Pinned by tests that do not reuse this file's formulas: brute-force prefix
+counting, exhaustive tiny beam sets, a PyTorch gather restating the pages'
+unpack, PyTorch scaled-dot-product attention on single-beam trees, closed
+forms (self-only attention, uniform scores, one-hot projections), GQA versus
+repeated-head MHA, and hand-worked accept cases under tests/golden/.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "pack_beams", "tree_mask", "mask_to_bits", "attention_per_beam",
+    "attention_packed", "lm_head_logits", "argmax_first", "unpack",
+    "greedy_accept", "verify_requests",
+]
+
+
+# ---------------------------------------------------------------- step 1 --
+def pack_beams(beams: np.ndarray) -> dict:
+    """Deduplicate shared prefixes of each request's beams with a literal trie.
+
+    [NEWS] "Dynamic tree attention" and [PAPER] abstract (2): the beams that
+    beam search returns share prefixes; the shared prefixes are found and
+    removed from the tokens the target verifies.  [TRT] PyTorch `unpack`:
+    the unpacker has shape [batch, beam_width, beam_length] and indexes
+    dimension 1 of the packed tensor.
+
+    A trie node is a distinct prefix beams[b, w, 0..l].  Nodes are numbered
+    in the order a beam-major scan first meets them (trie insertion order),
+    so a parent always precedes its children.
+
+    Returns int32 arrays: tokens [B,P] (pad -1), length [B], unpacker
+    [B,W,L], depth [B,P] (pad -1), src [B,P] = w*L+l of the first
+    occurrence (pad -1), with P = W*L.
+    """
+    beams = np.asarray(beams)
+    B, W, L = beams.shape
+    P = W * L
+    tokens = np.full((B, P), -1, np.int32)
+    depth = np.full((B, P), -1, np.int32)
+    src = np.full((B, P), -1, np.int32)
+    length = np.zeros(B, np.int32)
+    unpacker = np.zeros((B, W, L), np.int32)
+    for b in range(B):
+        child = {}  # (parent node or -1 for the virtual root, token) -> node
+        n = 0
+        for w in range(W):
+            cur = -1
+            for l in range(L):
+                key = (cur, int(beams[b, w, l]))
+                if key not in child:
+                    child[key] = n
+                    tokens[b, n] = beams[b, w, l]
+                    depth[b, n] = l
+                    src[b, n] = w * L + l
+                    n += 1
+                cur = child[key]
+                unpacker[b, w, l] = cur
+        length[b] = n
+    return {"tokens": tokens, "length": length, "unpacker": unpacker, "depth": depth, "src": src}
+
+
+def tree_mask(unpacker: np.ndarray, packed_len: np.ndarray) -> np.ndarray:
+    """Tree-causal mask, bool [B, P, P]: mask[b,p,q] iff q is p or an ancestor of p.
+
+    [SURV] SpecInfer "Token Tree Verifier": the tree is laid out in a
+    depth-first-compatible order and one topology-aware causal mask lets a
+    single kernel evaluate every path.  Node p = unpacker[b,w,l] has as
+    ancestors-or-self exactly the nodes unpacker[b,w,0..l] on its beam.
+    Rows and columns at or beyond packed_len are zero.
+    """
+    B, W, L = unpacker.shape
+    P = W * L
+    mask = np.zeros((B, P, P), dtype=bool)
+    for b in range(B):
+        for w in range(W):
+            for l in range(L):
+                p = unpacker[b, w, l]
+                for j in range(l + 1):
+                    mask[b, p, unpacker[b, w, j]] = True
+        n = int(packed_len[b])
+        mask[b, n:, :] = False
+        mask[b, :, n:] = False
+    return mask
+
+
+def mask_to_bits(mask: np.ndarray) -> np.ndarray:
+    """Bit-packed mask rows: uint32 [B, P, ceil(P/32)], bit (q % 32) of word q // 32."""
+    B, P, _ = mask.shape
+    nw = (P + 31) // 32
+    out = np.zeros((B, P, nw), dtype=np.uint32)
+    for q in range(P):
+        out[:, :, q // 32] |= (mask[:, :, q].astype(np.uint32) << np.uint32(q % 32))
+    return out
+
+
+# ---------------------------------------------------------------- step 2 --
+def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """softmax over the last axis of `scores` [..., T] applied to values [..., T, D]."""
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    e /= e.sum(axis=-1, keepdims=True)
+    return np.matmul(e[..., None, :], values)[..., 0, :]
+
+
+def attention_per_beam(q, k, v, k_cache, v_cache, kv_len, scale=None) -> np.ndarray:
+    """Causal attention of every candidate over its own beam alone (no dedup).
+
+    [TRT] intro and FAQ: the target verifies draft tokens from several
+    paths with tree-style attention; [NEWS] "Dynamic tree attention":
+    removing shared prefixes only reduces the data processed, so the result
+    must equal attending over each beam by itself.  This is that definition.
+
+    q [B,W,L,Hq,D]; k, v [B,W,L,Hkv,D]; k_cache, v_cache [B,Hkv,S,D];
+    kv_len [B].  For candidate (b,w,l) and head h with KV head
+    g = h // (Hq/Hkv): keys are k_cache[b,g,0:kv_len[b]] followed by
+    k[b,w,0..l,g]; scores are q.k * scale (default 1/sqrt(D)); softmax;
+    weighted sum of the matching values.  Returns fp64 [B,W,L,Hq,D].
+    """
+    q = np.asarray(q, np.float64)
+    B, W, L, Hq, D = q.shape
+    Hkv = k.shape[3]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.zeros((B, W, L, Hq, D), np.float64)
+    for b in range(B):
+        n = int(kv_len[b])
+        kc = np.asarray(k_cache[b, :, :n], np.float64)          # [Hkv, n, D]
+        vc = np.asarray(v_cache[b, :, :n], np.float64)
+        for w in range(W):
+            kb = np.asarray(k[b, w], np.float64)                 # [L, Hkv, D]
+            vb = np.asarray(v[b, w], np.float64)
+            for l in range(L):
+                qg = q[b, w, l].reshape(Hkv, G, D)               # head h = g*G + j
+                s_cache = np.matmul(qg, kc.transpose(0, 2, 1))    # [Hkv, G, n]
+                kn = kb[:l + 1].transpose(1, 0, 2)                # [Hkv, l+1, D]
+                vn = vb[:l + 1].transpose(1, 0, 2)
+                s_new = np.matmul(qg, kn.transpose(0, 2, 1))      # [Hkv, G, l+1]
+                scores = np.concatenate([s_cache, s_new], axis=-1) * scale
+                vals = np.concatenate([vc, vn], axis=1)           # [Hkv, n+l+1, D]
+                o = np.stack([_softmax_weighted_sum(scores[g], vals[g]) for g in range(Hkv)])
+                out[b, w, l] = o.reshape(Hq, D)
+    return out
+
+
+def attention_packed(q, k, v, k_cache, v_cache, kv_len, mask, packed_len, scale=None) -> np.ndarray:
+    """Tree attention over packed tokens with the tree-causal mask.
+
+    [SURV] "Token Tree Verifier": all paths in one pass under one mask.
+    q [B,P,Hq,D]; k, v [B,P,Hkv,D]; mask bool [B,P,P].  Packed query p sees
+    every cached key plus the packed keys q' with mask[b,p,q'].  Rows at or
+    beyond packed_len are zero.  Returns fp64 [B,P,Hq,D].
+    """
+    q = np.asarray(q, np.float64)
+    B, P, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.zeros((B, P, Hq, D), np.float64)
+    for b in range(B):
+        n = int(kv_len[b])
+        kc = np.asarray(k_cache[b, :, :n], np.float64)
+        vc = np.asarray(v_cache[b, :, :n], np.float64)
+        for p in range(int(packed_len[b])):
+            vis = np.nonzero(mask[b, p])[0]
+            qg = q[b, p].reshape(Hkv, G, D)
+            kn = np.asarray(k[b, vis], np.float64).transpose(1, 0, 2)   # [Hkv, nv, D]
+            vn = np.asarray(v[b, vis], np.float64).transpose(1, 0, 2)
+            scores = np.concatenate([np.matmul(qg, kc.transpose(0, 2, 1)),
+                                     np.matmul(qg, kn.transpose(0, 2, 1))], axis=-1) * scale
+            vals = np.concatenate([vc, vn], axis=1)
+            o = np.stack([_softmax_weighted_sum(scores[g], vals[g]) for g in range(Hkv)])
+            out[b, p] = o.reshape(Hq, D)
+    return out
+
+
+# ---------------------------------------------------------------- step 3 --
+def lm_head_logits(hidden: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """logits = hidden . weight^T in fp64; weight is [V, K] (nn.Linear layout).
+
+    [NEWS] benchmark paragraph: verification is greedy decoding, so each
+    candidate needs the target's logits over the vocabulary.
+    """
+    h = np.asarray(hidden, np.float64)
+    w = np.asarray(weight, np.float64)
+    return np.matmul(h, w.T)
+
+
+def argmax_first(logits: np.ndarray) -> np.ndarray:
+    """Index of the largest logit along the last axis; the lowest index wins ties."""
+    return np.argmax(logits, axis=-1).astype(np.int32)
+
+
+def unpack(packed: np.ndarray, unpacker: np.ndarray) -> np.ndarray:
+    """[TRT] PyTorch `unpack`: out[b,w,l,:] = packed[b, unpacker[b,w,l], :].
+
+    packed [B,P,X] (rank 3), unpacker [B,W,L] -> [B,W,L,X].
+    """
+    packed = np.asarray(packed)
+    assert packed.ndim == 3
+    B, W, L = unpacker.shape
+    out = np.empty((B, W, L, packed.shape[2]), dtype=packed.dtype)
+    for b in range(B):
+        for w in range(W):
+            for l in range(L):
+                out[b, w, l] = packed[b, unpacker[b, w, l]]
+    return out
+
+
+# ---------------------------------------------------------------- step 4 --
+def greedy_accept(beams: np.ndarray, target: np.ndarray) -> dict:
+    """Greedy acceptance of the best beam plus one bonus token.
+
+    [TRT] intro: tokens are verified and the best path is accepted before
+    the next drafting round; [NEWS] greedy decoding; [NEWS] "RNN draft
+    model": the drafter starts from the target's own initial token, so beam
+    position 0 is that token and position j+1 is a draft that the target's
+    prediction at position j must equal.
+
+    target [B,W,L] = target argmax at every candidate position.  For beam
+    w, n_w is the largest n <= L-1 with beams[b,w,j+1] == target[b,w,j] for
+    all j < n.  The best beam is the lowest index with the largest n_w; the
+    accepted tokens are beams[b,best,1..n] followed by the bonus
+    target[b,best,n].
+
+    Returns int32: match_len [B,W], best_beam [B], accept_len [B] (= n),
+    accepted_tokens [B,L] (n drafts + bonus, pad -1).
+    """
+    B, W, L = beams.shape
+    match_len = np.zeros((B, W), np.int32)
+    best_beam = np.zeros(B, np.int32)
+    accept_len = np.zeros(B, np.int32)
+    accepted = np.full((B, L), -1, np.int32)
+    for b in range(B):
+        best, best_n = 0, -1
+        for w in range(W):
+            n = 0
+            while n < L - 1 and beams[b, w, n + 1] == target[b, w, n]:
+                n += 1
+            match_len[b, w] = n
+            if n > best_n:
+                best, best_n = w, n
+        best_beam[b] = best
+        accept_len[b] = best_n
+        toks = [int(t) for t in beams[b, best, 1:best_n + 1]] + [int(target[b, best, best_n])]
+        accepted[b, :len(toks)] = toks
+    return {"match_len": match_len, "best_beam": best_beam, "accept_len": accept_len,
+            "accepted_tokens": accepted}
+
+
+# ------------------------------------------------------------- the step --
+def verify_requests(beams, q_unp, k_unp, v_unp, k_cache, v_cache, kv_len, hidden_unp, weight,
+                    scale=None, want_logits=True) -> dict:
+    """One verification step on a set of requests, in the unpacked definition.
+
+    Everything is per candidate (b,w,l) with no deduplication except the
+    pack/mask outputs, which are reported for comparison.  Arrays are
+    indexed by position in the given set.
+    """
+    pk = pack_beams(beams)
+    mask = tree_mask(pk["unpacker"], pk["length"])
+    attn = attention_per_beam(q_unp, k_unp, v_unp, k_cache, v_cache, kv_len, scale)
+    logits = lm_head_logits(hidden_unp, weight)
+    target = argmax_first(logits)
+    acc = greedy_accept(beams, target)
+    out = {"pack": pk, "mask": mask, "mask_bits": mask_to_bits(mask), "attn": attn,
+           "target": target, **acc}
+    if want_logits:
+        out["logits"] = logits
+    return out
