@@ -1,0 +1,225 @@
+"""Throughput of one ReDrafter verification step on one MI355X.
+
+A step is the whole path: pack -> tree mask -> tree attention -> projection
++ argmax -> unpack + greedy accept, enqueued through the C ABI on one
+stream.  Inputs are resident in HBM before timing starts.  The workload
+defaults to the bf16 Llama-style setting (B=8, W=8, L=5, 32x128 heads,
+1024 cached tokens, vocabulary 32000); other settings are selectable.
+
+Prints one JSON line with the step throughput (candidate tokens/s), the
+roofline position of the dominant call and of tree attention (HIP events
+on the launch stream, inside the timed region), and the CPU oracle timed
+on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama_mha")
+    ap.add_argument("--variant", choices=["full", "argmax-only"], default="full")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0,
+                    help="rotate input sets until they exceed this many MB (defeats cache residency)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="requests in the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool):
+    """Algorithmic traffic and work of each call (valid packed rows only; caches read once)."""
+    R = int(plen.sum())
+    e = 2 if cfg.dtype == "bf16" else 4
+    D, Hq, Hkv, K, V = cfg.D, cfg.Hq, cfg.Hkv, cfg.hidden, cfg.V
+    cache = int(kv_len.sum()) * Hkv * D * 2 * e
+    attn_bytes = cache + R * Hkv * D * 2 * e + R * Hq * D * 2 * e
+    # visible keys per query: cache + ancestors (depth+1 ~ counted as the full tree path)
+    attn_flops = 4 * D * Hq * (int((plen * kv_len).sum()))
+    lm_bytes = V * K * e + R * K * e + (R * V * e if want_logits else 0)
+    lm_flops = 2 * R * V * K
+    cand = cfg.B * cfg.W * cfg.L
+    unpack_bytes = (R * V * e + cand * V * e) if want_logits else 0
+    return {"attention": (attn_bytes, attn_flops), "lm_head": (lm_bytes, lm_flops), "unpack": (unpack_bytes, 0)}
+
+
+def cpu_baseline(cfg, seed: int, sample: int):
+    """The oracle as it stands, on `sample` requests of the same workload."""
+    import oracle
+    from synthetic import draw_beams, unpacked_node_tensors, kv_cache, lm_weight
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sub = cfg.with_(B=sample)
+    beams = draw_beams(sub, seed)
+    nodes = unpacked_node_tensors(sub, seed, beams)
+    kc = np.stack([kv_cache(sub, seed, b)[0] for b in range(sample)])
+    vc = np.stack([kv_cache(sub, seed, b)[1] for b in range(sample)])
+    w = lm_weight(sub, seed)
+    kv = np.full(sample, cfg.S, np.int32)
+    t0 = time.perf_counter()
+    res = oracle.verify_requests(beams, nodes["q"], nodes["k"], nodes["v"], kc, vc, kv, nodes["hidden"], w)
+    oracle.unpack(np.zeros((sample, cfg.P_max, 1)), res["pack"]["unpacker"])
+    dt = time.perf_counter() - t0
+    cand = sample * cfg.W * cfg.L
+    return {"value": cand / dt, "unit": "candidate tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample} of {cfg.B} requests of {cfg.name} (full step per request, fp64 numpy), "
+                      f"{dt:.1f} s"}
+
+
+def make_sets(cfg, n_sets, seed, dev, dt):
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    B, P = cfg.B, cfg.P_max
+
+    def rn(shape, scale=1.0):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * scale).to(dt)
+
+    sets = []
+    for _ in range(n_sets):
+        sets.append({
+            "q": rn((B, P, cfg.Hq, cfg.D)), "k_new": rn((B, P, cfg.Hkv, cfg.D)), "v_new": rn((B, P, cfg.Hkv, cfg.D)),
+            "k_cache": rn((B, cfg.Hkv, cfg.S, cfg.D)), "v_cache": rn((B, cfg.Hkv, cfg.S, cfg.D)),
+            "hidden": rn((B, P, cfg.hidden)), "weight": rn((cfg.V, cfg.hidden), 0.02),
+        })
+    return sets
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the verification path shards by "
+              f"request with no exchange, and this build runs on a single device", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tree_attention_verification_rd_amd as rd
+    from synthetic import get_config, base_seed, draw_beams, kv_lengths
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.config)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    esz = 2 if cfg.dtype == "bf16" else 4
+    seed = base_seed(cfg)
+    full = args.variant == "full"
+
+    beams = torch.from_numpy(draw_beams(cfg, seed)).to(dev)
+    kv_len_np = kv_lengths(cfg)
+    kv_len = torch.from_numpy(kv_len_np).to(dev)
+    B, P = cfg.B, cfg.P_max
+    set_bytes = esz * (B * P * (2 * cfg.Hq + 2 * cfg.Hkv) * cfg.D + 2 * B * cfg.Hkv * cfg.S * cfg.D
+                       + B * P * cfg.hidden + cfg.V * cfg.hidden)
+    n_sets = int(min(8, max(2, np.ceil(args.rotate_mb * 1e6 / set_bytes))))
+    sets = make_sets(cfg, n_sets, seed, dev, dt)
+    bufs = rd.VerifyBuffers(B, cfg.W, cfg.L, cfg.Hq, cfg.Hkv, cfg.D, cfg.S, cfg.hidden, cfg.V, dt, dev,
+                            want_logits=full)
+    pk = bufs.pack
+
+    def step(s, ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        rd.rd_pack_beams(beams, packed_tokens=pk["tokens"], packed_len=pk["length"], unpacker=pk["unpacker"],
+                         packed_depth=pk["depth"], packed_src=pk["src"])
+        rec(1)
+        rd.rd_tree_mask(pk["unpacker"], pk["length"], mask=bufs.mask)
+        rec(2)
+        rd.rd_tree_attention(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], kv_len, bufs.mask,
+                             pk["length"], out=bufs.attn, workspace=bufs.attn_ws)
+        rec(3)
+        rd.rd_lm_head_argmax(s["hidden"], pk["length"], s["weight"], want_logits=full, logits=bufs.logits,
+                             argmax=bufs.argmax, workspace=bufs.lm_ws)
+        rec(4)
+        rd.rd_unpack_accept(beams, pk["unpacker"], bufs.argmax, bufs.logits if full else None,
+                            unpacked=bufs.unpacked, **bufs.accept)
+        rec(5)
+
+    for i in range(args.warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        step(sets[i % n_sets], evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_gpu = t_start.elapsed_time(t_end) / K
+    ms_per_step = max(wall * 1e3 / K, ms_gpu)
+    names = ["pack", "mask", "attention", "lm_head", "unpack_accept"]
+    per_call_us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]) * 1e3) for j, n in enumerate(names)}
+
+    plen = pk["length"].cpu().numpy()
+    work = step_bytes_and_flops(cfg, plen, kv_len_np, full)
+    cand = B * cfg.W * cfg.L
+
+    def roof(call, bound):
+        nbytes, flops = work[call]
+        t = per_call_us[call] * 1e-6
+        if bound == "hbm":
+            ach = nbytes / t / 1e9
+            return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "algorithmic_bytes": int(nbytes), "avg_us": round(per_call_us[call], 2)}
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = flops / t / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "algorithmic_flops": int(flops),
+                "avg_us": round(per_call_us[call], 2)}
+
+    def bound_of(call):
+        nbytes, flops = work[call]
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        return "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12) else "mfma"
+
+    dominant = max(("attention", "lm_head"), key=lambda c: per_call_us[c])
+    line = {
+        "metric": "verified candidate tokens/sec per verify step; attention HBM GB/s % peak",
+        "value": round(cand / (ms_per_step * 1e-3), 1),
+        "unit": "candidate tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded beams from the workload's share rule; N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": cfg.name, "B": B, "W": cfg.W, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
+                   "S": cfg.S, "V": cfg.V, "hidden": cfg.hidden, "variant": args.variant,
+                   "packed_tokens": int(plen.sum()), "candidates": cand, "input_sets_rotated": n_sets},
+        "roofline": {"kernel": f"rd_{'lm_head_argmax' if dominant == 'lm_head' else 'tree_attention'}",
+                     **roof(dominant, bound_of(dominant))},
+        "attention_hbm": {"kernel": "rd_tree_attention", **roof("attention", "hbm")},
+        "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
+        "gpu_ms_per_step": round(ms_gpu, 4),
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or (B if cfg.candidates <= 400 else 2)
+        line["cpu_baseline"] = cpu_baseline(cfg, seed, min(sample, B))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

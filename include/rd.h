@@ -1,0 +1,202 @@
+/*
+ * rd.h -- C ABI of the ReDrafter verification-step library (librd.so, gfx950).
+ *
+ * One verification step of Recurrent Drafting checks the W beam-search
+ * candidates of length L of each of B requests against the target model in a
+ * single pass: (1) shared prefixes are removed into a packed token tree with
+ * an unpacker index and a tree-causal mask, (2) the packed tokens attend to
+ * the request's KV cache and their tree ancestors, (3) the outputs are
+ * projected to logits, reduced to the target's greedy choice and unpacked to
+ * [B,W,L,V], (4) the beam with the longest prefix that agrees with the target
+ * is accepted together with one bonus token.
+ *
+ * Sources, cited by page title and section:
+ *   [TRT]   "ReDrafter in NVIDIA TensorRT-LLM" blog: intro; "Inflight-batching
+ *           Compatible Engine"; "Implementing in-Engine Validation and
+ *           Drafting" (the PyTorch `unpack` and TensorRT-LLM `_unpack_beams`
+ *           listings).
+ *   [NEWS]  Apple/NVIDIA ReDrafter news article: "RNN draft model", "Dynamic
+ *           tree attention", greedy-decoding benchmark paragraph.
+ *   [PAPER] "Recurrent Drafter for Fast Speculative Decoding in Large Language
+ *           Models", abstract point (2).
+ *   [SURV]  "Accelerating LLM inference with speculative decoding" survey,
+ *           SpecInfer "Token Tree Verifier".
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (dev) are device memory owned by the caller; the
+ *     library never allocates, frees or retains them past the call.  Arrays
+ *     are dense and row-major in the shapes given; int32 unless stated.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns without synchronising the host.  Results are
+ *     valid once the stream reaches that point.
+ *   - P_max == W*L is the static packed width: no call reads packed lengths
+ *     back to the host.
+ *   - Status: RD_OK, or a negative code from host-side validation made
+ *     before anything is launched (RD_E_ARG: null required pointer, negative
+ *     size, inconsistent shape; RD_E_UNSUPPORTED: size or dtype outside the
+ *     limits below; RD_E_WORKSPACE: workspace smaller than its query), or
+ *     RD_E_HIP when a launch fails.
+ *   - Empty inputs (any of B, W, L == 0) return RD_OK with nothing launched:
+ *     [TRT] "Inflight-batching Compatible Engine" requires every operator on
+ *     the generation path to accept empty tensors.
+ *   - Device-side contents (kv_len <= S_max, unpacker values in [0,P_max))
+ *     are trusted as produced by rd_pack_beams; kernels clamp every index
+ *     they derive from them so a bad value cannot address outside the
+ *     arrays, but the results are then unspecified.
+ *   - Results are deterministic: identical inputs give bit-identical outputs
+ *     (no floating-point atomics, fixed reduction orders).
+ *   - The library keeps no state between calls and is safe to call from
+ *     several host threads on different streams.
+ */
+#ifndef RD_H
+#define RD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *rd_stream_t; /* hipStream_t */
+
+enum rd_status_code {
+    RD_OK = 0,
+    RD_E_ARG = -1,
+    RD_E_UNSUPPORTED = -2,
+    RD_E_WORKSPACE = -3,
+    RD_E_HIP = -4
+};
+
+enum rd_dtype {
+    RD_F32 = 0,  /* IEEE binary32 */
+    RD_BF16 = 1  /* bfloat16; computed with fp32 accumulation */
+};
+
+#define RD_MAX_BEAMS 64      /* W limit: one wavefront lane per beam */
+#define RD_MAX_BEAM_LEN 16   /* L limit */
+
+/* Human-readable name of a status code (static storage). */
+const char *rd_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int rd_version(void);
+
+/*
+ * Step 1 -- pack: remove shared prefixes across each request's beams.
+ * [NEWS] "Dynamic tree attention", [PAPER] abstract (2): beams share
+ * prefixes; each distinct prefix beams[b,w,0..l] is verified once.
+ * [TRT] PyTorch `unpack`: unpacker[b,w,l] indexes dimension 1 of the packed
+ * tensor.  Packed slots are numbered in the order a beam-major scan first
+ * meets each prefix, so a parent precedes its children.
+ *
+ *   beams         (dev) [B,W,L]  token ids (any int32 values)
+ *   packed_tokens (dev) [B,P_max] token of each slot, -1 past packed_len
+ *   packed_len    (dev) [B]      number of distinct prefixes of request b
+ *   unpacker      (dev) [B,W,L]  slot of candidate (w,l), in [0,packed_len)
+ *   packed_depth  (dev) [B,P_max] depth l of each slot, -1 padding; may be NULL
+ *   packed_src    (dev) [B,P_max] w*L+l of each slot's first occurrence, -1
+ *                                 padding; may be NULL
+ * Limits: W <= RD_MAX_BEAMS, L <= RD_MAX_BEAM_LEN.
+ */
+int rd_pack_beams(const int32_t *beams, int B, int W, int L,
+                  int32_t *packed_tokens, int32_t *packed_len, int32_t *unpacker,
+                  int32_t *packed_depth, int32_t *packed_src, rd_stream_t stream);
+
+/*
+ * Step 1b -- tree-causal mask.  [SURV] SpecInfer "Token Tree Verifier": one
+ * topology-aware causal mask lets every path of the tree be evaluated in one
+ * kernel.  Bit q of row p is set iff slot q is slot p or one of its
+ * ancestors; rows and columns at or past packed_len are zero.
+ *
+ *   unpacker, packed_len (dev) as produced by rd_pack_beams
+ *   mask (dev) uint32 [B,P_max,ceil(P_max/32)]: bit (q%32) of word q/32.
+ */
+int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int W, int L,
+                 uint32_t *mask, rd_stream_t stream);
+
+/* Bytes of device workspace rd_tree_attention needs for these sizes (may be 0). */
+size_t rd_tree_attention_workspace_size(int dtype, int B, int P_max, int Hq, int Hkv, int D,
+                                        int S_max);
+
+/*
+ * Step 2 -- tree attention.  [TRT] intro and FAQ: the target verifies draft
+ * tokens from several paths at once with tree-style attention; [NEWS]
+ * "Dynamic tree attention": deduplication only removes repeated work, so
+ * packed slot p = unpacker[b,w,l] must yield the output of causal
+ * attention over beam w alone.  For packed query p < packed_len[b] and
+ * head h, with KV head g = h / (Hq/Hkv): keys are k_cache[b,g,0:kv_len[b]]
+ * (all visible) followed by k_new[b,q,g] for every slot q whose bit is set
+ * in mask row p; softmax(q.k * scale) weights the matching values.
+ *
+ *   dtype        RD_BF16 (fp32 softmax and accumulation, bf16 output) or RD_F32
+ *   q       (dev) [B,P_max,Hq,D]   packed queries (already position-encoded)
+ *   k_new, v_new (dev) [B,P_max,Hkv,D] packed keys/values
+ *   k_cache, v_cache (dev) [B,Hkv,S_max,D]
+ *   kv_len  (dev) [B]  cached tokens of request b, 0 <= kv_len[b] <= S_max
+ *   mask, packed_len (dev) from rd_tree_mask / rd_pack_beams
+ *   scale   softmax scale; 0 selects 1/sqrt(D)
+ *   out     (dev) [B,P_max,Hq,D]  rows at or past packed_len are written as 0
+ *   ws      (dev) workspace of ws_bytes >= rd_tree_attention_workspace_size()
+ * Limits: D in {64,128}, Hq % Hkv == 0, P_max <= RD_MAX_BEAMS*RD_MAX_BEAM_LEN.
+ */
+int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v_new,
+                      const void *k_cache, const void *v_cache, const int32_t *kv_len,
+                      const uint32_t *mask, const int32_t *packed_len,
+                      int B, int P_max, int Hq, int Hkv, int D, int S_max, float scale,
+                      void *out, void *ws, size_t ws_bytes, rd_stream_t stream);
+
+/* Bytes of device workspace rd_lm_head_argmax needs for these sizes. */
+size_t rd_lm_head_workspace_size(int dtype, int B, int P_max, int K, int V);
+
+/*
+ * Step 3 -- output projection and greedy target token.  [NEWS] greedy
+ * decoding: the target's choice at every packed position is the argmax of
+ * hidden . weight^T, taken on the fp32 accumulators (never on rounded
+ * logits), lowest vocabulary id on ties.  Only rows p < packed_len[b] are
+ * computed.
+ *
+ *   hidden  (dev) [B,P_max,K]  (dtype)
+ *   packed_len (dev) [B], or NULL meaning every row is valid
+ *   weight  (dev) [V,K]  (nn.Linear layout, dtype)
+ *   logits  (dev) [B,P_max,V] in dtype, or NULL to skip writing them; rows
+ *           past packed_len are left untouched
+ *   argmax  (dev) [B,P_max]  -1 past packed_len
+ *   ws      (dev) workspace of ws_bytes >= rd_lm_head_workspace_size()
+ * Limits: K % 8 == 0 for RD_BF16.
+ */
+int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len,
+                      const void *weight, int B, int P_max, int K, int V,
+                      void *logits, int32_t *argmax, void *ws, size_t ws_bytes,
+                      rd_stream_t stream);
+
+/*
+ * Steps 3b and 4 -- unpack and greedy accept.
+ * Unpack ([TRT] PyTorch `unpack` / TensorRT-LLM `_unpack_beams`):
+ *   unpacked[b,w,l,:] = packed[b, unpacker[b,w,l], :] with rows of row_len
+ *   elements of dtype; skipped when packed or unpacked is NULL.
+ * Accept ([TRT] intro: verify, then accept the best path before the next
+ * drafting round; [NEWS] greedy decoding; [NEWS] "RNN draft model": beam
+ * position 0 is the target's own initial token):
+ *   a[w,l] = packed_argmax[b, unpacker[b,w,l]];
+ *   match_len[b,w] = largest n <= L-1 with beams[b,w,j+1] == a[w,j], j < n;
+ *   best_beam[b]   = lowest w with the largest match_len;
+ *   accept_len[b]  = n = match_len[b,best];
+ *   accepted_tokens[b,:] = beams[b,best,1..n], then a[best,n], then -1.
+ *
+ *   beams, unpacker (dev) [B,W,L]; packed_argmax (dev) [B,P_max]
+ *   packed (dev) [B,P_max,row_len] or NULL; unpacked (dev) [B,W,L,row_len] or NULL
+ *   match_len (dev) [B,W]; best_beam, accept_len (dev) [B];
+ *   accepted_tokens (dev) [B,L]
+ */
+int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker,
+                     const int32_t *packed_argmax, const void *packed, void *unpacked,
+                     int dtype, int64_t row_len, int B, int W, int L,
+                     int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
+                     int32_t *accepted_tokens, rd_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RD_H */

@@ -1,0 +1,82 @@
+"""The C-ABI library loads and exports every entry point include/rd.h declares (CPU only).
+
+Only calls that return before touching the HIP runtime are made here:
+status strings, the version, and host-side argument validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verification_rd_amd as rd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("rd_pack_beams", "rd_tree_mask", "rd_tree_attention", "rd_lm_head_argmax", "rd_unpack_accept"):
+        assert n in names
+    assert set(names) == set(rd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(rd.lib_path()), "build librd.so first (python __graft_entry__.py)"
+    lib = ctypes.CDLL(rd.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = rd.load_library()
+    for code, word in ((0, b"RD_OK"), (-1, b"RD_E_ARG"), (-2, b"RD_E_UNSUPPORTED"), (-3, b"RD_E_WORKSPACE"),
+                       (-4, b"RD_E_HIP")):
+        assert lib.rd_status_string(code).startswith(word)
+    assert lib.rd_version() >= 100
+
+
+def test_host_side_validation_without_device():
+    lib = rd.load_library()
+    null = None
+    # negative sizes -> RD_E_ARG before any launch
+    assert lib.rd_pack_beams(null, -1, 4, 4, null, null, null, null, null, null) == -1
+    assert lib.rd_tree_mask(null, null, 2, -3, 4, null, null) == -1
+    # empty batches are no-ops, even with null pointers
+    assert lib.rd_pack_beams(null, 0, 4, 4, null, null, null, null, null, null) == 0
+    assert lib.rd_pack_beams(null, 3, 0, 4, null, null, null, null, null, null) == 0
+    assert lib.rd_unpack_accept(null, null, null, null, null, 1, 8, 2, 4, 0, null, null, null, null, null) == 0
+    # missing required pointers
+    assert lib.rd_pack_beams(null, 2, 4, 4, null, null, null, null, null, null) == -1
+    # limits: W > 64, L > 16 (pointers are not dereferenced on the host)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.rd_pack_beams(fake, 2, 65, 4, fake, fake, fake, null, null, null) == -2
+    assert lib.rd_pack_beams(fake, 2, 4, 17, fake, fake, fake, null, null, null) == -2
+    # attention: unsupported dtype / head dim, bad head grouping, negative scale
+    args = [fake] * 8
+    assert lib.rd_tree_attention(7, *args, 2, 8, 4, 4, 128, 64, 0.0, fake, fake, 0, null) == -2
+    assert lib.rd_tree_attention(1, *args, 2, 8, 4, 4, 96, 64, 0.0, fake, fake, 0, null) == -2
+    assert lib.rd_tree_attention(1, *args, 2, 8, 6, 4, 128, 64, 0.0, fake, fake, 0, null) == -1
+    assert lib.rd_tree_attention(1, *args, 2, 8, 4, 4, 128, 64, -1.0, fake, fake, 0, null) == -1
+    assert lib.rd_tree_attention(1, *args, 0, 8, 4, 4, 128, 64, 0.0, fake, fake, 0, null) == 0
+    # projection: K not a multiple of 8 in bf16, unknown dtype, empty
+    assert lib.rd_lm_head_argmax(1, fake, fake, fake, 2, 8, 100, 50, fake, fake, fake, 1 << 20, null) == -2
+    assert lib.rd_lm_head_argmax(5, fake, fake, fake, 2, 8, 128, 50, fake, fake, fake, 1 << 20, null) == -2
+    assert lib.rd_lm_head_argmax(1, fake, fake, fake, 0, 8, 128, 50, fake, fake, fake, 0, null) == 0
+    # unpack/accept: unknown dtype
+    assert lib.rd_unpack_accept(fake, fake, fake, fake, fake, 9, 8, 2, 4, 3, fake, fake, fake, fake, null) == -2
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    monkeypatch.setattr(rd, "_lib", None)
+    monkeypatch.setattr(rd, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        rd.load_library()

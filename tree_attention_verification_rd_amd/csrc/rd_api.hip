@@ -1,0 +1,162 @@
+// C ABI of librd: argument validation and launch of the step kernels.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/rd.h"
+#include "rd_internal.h"
+
+namespace rd {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace rd
+
+namespace {
+
+hipStream_t as_stream(rd_stream_t s) { return static_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RD_OK : RD_E_HIP; }
+
+bool beam_shape_ok(int B, int W, int L) { return B >= 0 && W >= 0 && L >= 0; }
+bool beam_shape_supported(int W, int L) { return W <= rd::kMaxBeams && L <= rd::kMaxBeamLen; }
+
+}  // namespace
+
+extern "C" {
+
+const char *rd_status_string(int status) {
+    switch (status) {
+        case RD_OK: return "RD_OK";
+        case RD_E_ARG: return "RD_E_ARG: invalid argument (null pointer, negative or inconsistent size)";
+        case RD_E_UNSUPPORTED: return "RD_E_UNSUPPORTED: size or dtype outside the library's limits";
+        case RD_E_WORKSPACE: return "RD_E_WORKSPACE: workspace smaller than the size query returned";
+        case RD_E_HIP: return "RD_E_HIP: a HIP launch failed";
+        default: return "unknown rd status";
+    }
+}
+
+int rd_version(void) { return 100; }
+
+int rd_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *packed_tokens, int32_t *packed_len,
+                  int32_t *unpacker, int32_t *packed_depth, int32_t *packed_src, rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L)) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!beams || !packed_tokens || !packed_len || !unpacker) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    return hip_status(rd::launch_pack_beams(beams, B, W, L, packed_tokens, packed_len, unpacker, packed_depth,
+                                            packed_src, as_stream(stream)));
+}
+
+int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int W, int L, uint32_t *mask,
+                 rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L)) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!unpacker || !packed_len || !mask) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    return hip_status(rd::launch_tree_mask(unpacker, packed_len, B, W, L, mask, as_stream(stream)));
+}
+
+static int attn_check(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max) {
+    if (B < 0 || P_max < 0 || Hq < 0 || Hkv < 0 || D < 0 || S_max < 0) return RD_E_ARG;
+    if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    if (B == 0 || P_max == 0 || Hq == 0) return RD_OK;
+    if (Hkv == 0 || Hq % Hkv != 0) return RD_E_ARG;
+    if (D != 64 && D != 128) return RD_E_UNSUPPORTED;
+    if (P_max > rd::kMaxBeams * rd::kMaxBeamLen) return RD_E_UNSUPPORTED;
+    // bf16 kernels address one request's packed rows and one (request, KV
+    // head) cache slab through 31-bit buffer offsets
+    if (dtype == RD_BF16 && (static_cast<long long>(P_max) * Hkv * D * 2 > 0x7FFFFFFFLL ||
+                             static_cast<long long>(S_max) * D * 2 > 0x7FFFFFFFLL))
+        return RD_E_UNSUPPORTED;
+    return RD_OK;
+}
+
+size_t rd_tree_attention_workspace_size(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max) {
+    if (attn_check(dtype, B, P_max, Hq, Hkv, D, S_max) != RD_OK || B == 0 || P_max == 0 || Hq == 0) return 0;
+    return rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, S_max).ws_bytes;
+}
+
+int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                      const void *v_cache, const int32_t *kv_len, const uint32_t *mask, const int32_t *packed_len,
+                      int B, int P_max, int Hq, int Hkv, int D, int S_max, float scale, void *out, void *ws,
+                      size_t ws_bytes, rd_stream_t stream) {
+    const int chk = attn_check(dtype, B, P_max, Hq, Hkv, D, S_max);
+    if (chk != RD_OK) return chk;
+    if (B == 0 || P_max == 0 || Hq == 0) return RD_OK;
+    if (!q || !k_new || !v_new || !kv_len || !mask || !packed_len || !out) return RD_E_ARG;
+    if (S_max > 0 && (!k_cache || !v_cache)) return RD_E_ARG;
+    if (!(scale >= 0.f) || scale != scale) return RD_E_ARG;
+    const rd::AttnPlan plan = rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, S_max);
+    if (ws_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && !ws)) return RD_E_WORKSPACE;
+    return hip_status(rd::launch_attention(dtype, plan, q, k_new, v_new, k_cache, v_cache, kv_len, mask, packed_len,
+                                           B, P_max, Hq, Hkv, D, S_max, scale, out, ws, as_stream(stream)));
+}
+
+static int lm_check(int dtype, int B, int P_max, int K, int V) {
+    if (B < 0 || P_max < 0 || K < 0 || V < 0) return RD_E_ARG;
+    if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    if (B == 0 || P_max == 0) return RD_OK;
+    if (K == 0 || V == 0) return RD_E_ARG;
+    if (dtype == RD_BF16 && K % 8 != 0) return RD_E_UNSUPPORTED;
+    if (static_cast<long long>(B) * P_max > (1LL << 30)) return RD_E_UNSUPPORTED;
+    // bf16 kernels address the hidden rows and each wavefront's weight rows
+    // through 31-bit buffer offsets
+    if (dtype == RD_BF16 && static_cast<long long>(B) * P_max * K * 2 > 0x7FFFFFFFLL) return RD_E_UNSUPPORTED;
+    return RD_OK;
+}
+
+size_t rd_lm_head_workspace_size(int dtype, int B, int P_max, int K, int V) {
+    if (lm_check(dtype, B, P_max, K, V) != RD_OK || B == 0 || P_max == 0) return 0;
+    return rd::plan_lm_head(dtype, B, P_max, K, V).ws_bytes;
+}
+
+int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, const void *weight, int B,
+                      int P_max, int K, int V, void *logits, int32_t *argmax, void *ws, size_t ws_bytes,
+                      rd_stream_t stream) {
+    const int chk = lm_check(dtype, B, P_max, K, V);
+    if (chk != RD_OK) return chk;
+    if (B == 0 || P_max == 0) return RD_OK;
+    if (!hidden || !weight || !argmax) return RD_E_ARG;
+    const rd::LmPlan plan = rd::plan_lm_head(dtype, B, P_max, K, V);
+    if (ws_bytes < plan.ws_bytes || !ws) return RD_E_WORKSPACE;
+    return hip_status(rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P_max, K, V, logits, argmax,
+                                         ws, as_stream(stream)));
+}
+
+int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *packed_argmax, const void *packed,
+                     void *unpacked, int dtype, int64_t row_len, int B, int W, int L, int32_t *match_len,
+                     int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens, rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L) || row_len < 0) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!beams || !unpacker || !packed_argmax || !match_len || !best_beam || !accept_len || !accepted_tokens)
+        return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    hipStream_t s = as_stream(stream);
+    if (packed && unpacked && row_len > 0) {
+        const int64_t row_bytes = row_len * (dtype == RD_F32 ? 4 : 2);
+        const int64_t rows = static_cast<int64_t>(B) * W * L;
+        const int64_t chunks = (row_bytes + 1023) / 1024;  // upper bound on blocks per row
+        if (rows * chunks * 256 >= (1LL << 32)) return RD_E_UNSUPPORTED;
+        const hipError_t e = rd::launch_unpack(packed, unpacked, unpacker, row_bytes, B, W, L, s);
+        if (e != hipSuccess) return RD_E_HIP;
+    }
+    return hip_status(rd::launch_accept(beams, unpacker, packed_argmax, B, W, L, match_len, best_beam, accept_len,
+                                        accepted_tokens, s));
+}
+
+}  // extern "C"

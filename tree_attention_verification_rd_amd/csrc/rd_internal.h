@@ -1,0 +1,54 @@
+// Internal launchers shared by the C-ABI layer (rd_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rd {
+
+constexpr int kMaxBeams = 64;
+constexpr int kMaxBeamLen = 16;
+
+hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *tokens,
+                             int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
+                             hipStream_t stream);
+hipError_t launch_tree_mask(const int32_t *unpacker, const int32_t *plen, int B, int W, int L,
+                            uint32_t *mask, hipStream_t stream);
+
+// tree attention
+struct AttnPlan {
+    int nqblk;      // query-row blocks per (request, KV head)
+    int nsplit;     // KV-cache splits
+    int chunk;      // cache keys per split (multiple of the key tile)
+    size_t ws_bytes;
+};
+AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max);
+hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *k_new,
+                            const void *v_new, const void *k_cache, const void *v_cache,
+                            const int32_t *kv_len, const uint32_t *mask, const int32_t *plen,
+                            int B, int P_max, int Hq, int Hkv, int D, int S_max, float scale,
+                            void *out, void *ws, hipStream_t stream);
+
+// output projection + argmax
+struct LmPlan {
+    int rows_pad;   // B * P_max
+    int vtile;      // vocabulary columns per workgroup
+    int nvt;        // vocabulary tiles
+    size_t ws_bytes;
+};
+LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V);
+hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, const int32_t *plen,
+                          const void *weight, int B, int P_max, int K, int V, void *logits,
+                          int32_t *argmax, void *ws, hipStream_t stream);
+
+// unpack gather + accept
+hipError_t launch_unpack(const void *packed, void *unpacked, const int32_t *unpacker,
+                         int64_t row_bytes, int B, int W, int L, hipStream_t stream);
+hipError_t launch_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *pargmax,
+                         int B, int W, int L, int32_t *match_len, int32_t *best_beam,
+                         int32_t *accept_len, int32_t *accepted, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace rd

@@ -1,0 +1,156 @@
+// Step 1 (pack) and step 1b (tree-causal mask) kernels.
+//
+// Pack follows dynamic tree attention (Apple/NVIDIA ReDrafter news article,
+// "Dynamic tree attention"; ReDrafter paper abstract, point 2): a slot per
+// distinct prefix.  Slot order is the first occurrence in a beam-major scan.
+//
+// One wavefront per request, one lane per beam.  Lane w finds, by comparing
+// its beam against every earlier beam, m_w = the longest prefix it shares
+// with any earlier beam, and for each depth l the lowest beam whose prefix
+// of length l+1 equals its own.  Beam w contributes the L - m_w new slots
+// at depths m_w..L-1; their positions come from an exclusive prefix sum of
+// those counts across lanes, built from five ballots (one per bit of the
+// count) and popcounts of the lanes below.  Depths l < m_w reuse the slot
+// that the first sharing beam owns, read from that lane by a shuffle.
+#include "rd_common.h"
+#include "rd_internal.h"
+
+namespace rd {
+
+__global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ beams, int W, int L,
+                                                   int32_t *__restrict__ tokens,
+                                                   int32_t *__restrict__ plen,
+                                                   int32_t *__restrict__ unpacker,
+                                                   int32_t *__restrict__ depth,
+                                                   int32_t *__restrict__ src) {
+    __shared__ int32_t sb[kMaxBeams * kMaxBeamLen];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int P = W * L;
+    const int32_t *bb = beams + static_cast<size_t>(b) * P;
+    for (int i = lane; i < P; i += kWave) sb[i] = bb[i];
+    __syncthreads();
+
+    const bool active = lane < W;
+    int own[kMaxBeamLen];
+#pragma unroll
+    for (int l = 0; l < kMaxBeamLen; ++l) own[l] = (active && l < L) ? sb[lane * L + l] : 0;
+
+    int m = 0;                  // longest prefix shared with an earlier beam
+    int first[kMaxBeamLen];     // lowest beam sharing the prefix of length l+1
+#pragma unroll
+    for (int l = 0; l < kMaxBeamLen; ++l) first[l] = lane;
+
+    for (int v = 0; v < W; ++v) {  // uniform across the wave
+        int lcp = 0;
+        bool run = true;
+#pragma unroll
+        for (int l = 0; l < kMaxBeamLen; ++l) {
+            if (l < L) {
+                run = run && (sb[v * L + l] == own[l]);
+                lcp += run ? 1 : 0;
+            }
+        }
+        if (active && v < lane) {
+            m = max(m, lcp);
+#pragma unroll
+            for (int l = 0; l < kMaxBeamLen; ++l)
+                if (l < lcp && first[l] == lane) first[l] = v;
+        }
+    }
+
+    // exclusive prefix sum of new-slot counts over lanes, bit plane by bit plane
+    const int cnt = active ? (L - m) : 0;  // 0..16: five bits
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    int base = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bal = __ballot((cnt >> bit) & 1);
+        base += __popcll(bal & below) << bit;
+        total += __popcll(bal) << bit;
+    }
+
+    int32_t *urow = unpacker + (static_cast<size_t>(b) * W + (active ? lane : 0)) * L;
+#pragma unroll
+    for (int l = 0; l < kMaxBeamLen; ++l) {
+        if (l < L) {  // uniform: every lane takes part in the shuffles
+            const int owner = first[l];
+            const int owner_base = __shfl(base, owner, kWave);
+            const int owner_m = __shfl(m, owner, kWave);
+            if (active) urow[l] = owner_base + l - owner_m;
+        }
+    }
+
+    const size_t row = static_cast<size_t>(b) * P;
+    if (active) {
+#pragma unroll
+        for (int l = 0; l < kMaxBeamLen; ++l) {
+            if (l < L && l >= m) {
+                const int slot = base + l - m;
+                tokens[row + slot] = own[l];
+                if (depth) depth[row + slot] = l;
+                if (src) src[row + slot] = lane * L + l;
+            }
+        }
+    }
+    for (int s = total + lane; s < P; s += kWave) {
+        tokens[row + s] = -1;
+        if (depth) depth[row + s] = -1;
+        if (src) src[row + s] = -1;
+    }
+    if (lane == 0) plen[b] = total;
+}
+
+// Step 1b.  [SURV] SpecInfer "Token Tree Verifier": bit q of row p is set iff
+// slot q is p or an ancestor of p.  The parent of slot unpacker[w,l] is
+// unpacker[w,l-1]; every candidate that maps to a slot names the same
+// parent, so concurrent writers store the same value.  Each thread then
+// builds one mask word by walking at most L parent links.
+__global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ unpacker,
+                                                   const int32_t *__restrict__ plen, int W, int L,
+                                                   uint32_t *__restrict__ mask) {
+    __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
+    const int b = blockIdx.x;
+    const int P = W * L;
+    const int nw = (P + 31) / 32;
+    const int32_t *u = unpacker + static_cast<size_t>(b) * P;
+    for (int i = threadIdx.x; i < P; i += blockDim.x) parent[i] = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int l = i % L;
+        const int p = u[i];
+        if (p >= 0 && p < P) parent[p] = (l == 0) ? -1 : u[i - 1];
+    }
+    __syncthreads();
+    const int n = min(max(plen[b], 0), P);
+    uint32_t *out = mask + static_cast<size_t>(b) * P * nw;
+    for (int i = threadIdx.x; i < P * nw; i += blockDim.x) {
+        const int p = i / nw;
+        const int k = i % nw;
+        uint32_t word = 0;
+        if (p < n) {
+            int cur = p;
+            for (int step = 0; step < L && cur >= 0 && cur < P; ++step) {
+                if ((cur >> 5) == k && cur < n) word |= 1u << (cur & 31);
+                cur = parent[cur];
+            }
+        }
+        out[i] = word;
+    }
+}
+
+hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *tokens,
+                             int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(k_pack_beams, dim3(B), dim3(kWave), 0, stream, beams, W, L, tokens, plen,
+                       unpacker, depth, src);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_mask(const int32_t *unpacker, const int32_t *plen, int B, int W, int L,
+                            uint32_t *mask, hipStream_t stream) {
+    hipLaunchKernelGGL(k_tree_mask, dim3(B), dim3(256), 0, stream, unpacker, plen, W, L, mask);
+    return hipGetLastError();
+}
+
+}  // namespace rd

@@ -1,0 +1,117 @@
+// Step 3b (unpack gather) and step 4 (greedy accept) kernels.
+#include "rd_common.h"
+#include "rd_internal.h"
+
+namespace rd {
+
+// Unpack, as the PyTorch `unpack` listing of the TensorRT-LLM ReDrafter blog
+// ("Implementing in-Engine Validation and Drafting") defines it:
+// out[b,w,l,:] = packed[b, unpacker[b,w,l], :].  A streaming row copy: each
+// workgroup moves one chunk of one output row with UNROLL independent
+// vector loads in flight per thread.
+template <typename T, int UNROLL>
+__global__ __launch_bounds__(256) void k_unpack_rows(const T *__restrict__ packed, T *__restrict__ out,
+                                                     const int32_t *__restrict__ unpacker,
+                                                     int64_t row_elems, int P, int WL, int nchunks) {
+    const int64_t blk = blockIdx.x;
+    const int64_t row = blk / nchunks;
+    const int chunk = static_cast<int>(blk % nchunks);
+    const int64_t b = row / WL;
+    const int slot = min(max(unpacker[row], 0), P - 1);
+    const T *s = packed + (b * P + slot) * row_elems;
+    T *d = out + row * row_elems;
+    const int64_t base = static_cast<int64_t>(chunk) * (256 * UNROLL) + threadIdx.x;
+    T v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < row_elems) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < row_elems) __builtin_nontemporal_store(v[u], d + i);
+    }
+}
+
+// Greedy accept: one wavefront per request, one lane per beam.  Lane w walks
+// its beam while the draft at j+1 equals the target's choice at j; the best
+// beam is the max of the key (match length, -w) across lanes, so ties go to
+// the lowest beam.
+__global__ __launch_bounds__(64) void k_accept(const int32_t *__restrict__ beams,
+                                               const int32_t *__restrict__ unpacker,
+                                               const int32_t *__restrict__ pargmax, int W, int L,
+                                               int32_t *__restrict__ match_len,
+                                               int32_t *__restrict__ best_beam,
+                                               int32_t *__restrict__ accept_len,
+                                               int32_t *__restrict__ accepted) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int P = W * L;
+    const int32_t *am = pargmax + static_cast<size_t>(b) * P;
+    auto target_at = [&](int w, int l) {
+        const int slot = unpacker[(static_cast<size_t>(b) * W + w) * L + l];
+        return am[min(max(slot, 0), P - 1)];
+    };
+    int n = 0;
+    if (lane < W) {
+        const int32_t *bw = beams + (static_cast<size_t>(b) * W + lane) * L;
+        while (n < L - 1 && bw[n + 1] == target_at(lane, n)) ++n;
+        match_len[static_cast<size_t>(b) * W + lane] = n;
+    }
+    int key = (lane < W) ? ((n << 6) | (63 - lane)) : -1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_xor(key, off));
+    const int best = 63 - (key & 63);
+    const int nbest = key >> 6;
+    if (lane == 0) {
+        best_beam[b] = best;
+        accept_len[b] = nbest;
+    }
+    if (lane < L) {
+        int t = -1;
+        if (lane < nbest)
+            t = beams[(static_cast<size_t>(b) * W + best) * L + lane + 1];
+        else if (lane == nbest)
+            t = target_at(best, nbest);
+        accepted[static_cast<size_t>(b) * L + lane] = t;
+    }
+}
+
+hipError_t launch_unpack(const void *packed, void *unpacked, const int32_t *unpacker,
+                         int64_t row_bytes, int B, int W, int L, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(B) * W * L;
+    const int P = W * L;
+    const uintptr_t align = reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(unpacked);
+    constexpr int U = 4;
+    if (row_bytes % 16 == 0 && align % 16 == 0) {
+        const int64_t elems = row_bytes / 16;
+        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
+        hipLaunchKernelGGL((k_unpack_rows<u32x4, U>), dim3(static_cast<unsigned>(rows * nchunks)),
+                           dim3(256), 0, stream, static_cast<const u32x4 *>(packed),
+                           static_cast<u32x4 *>(unpacked), unpacker, elems, P, W * L, nchunks);
+    } else if (row_bytes % 4 == 0 && align % 4 == 0) {
+        const int64_t elems = row_bytes / 4;
+        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
+        hipLaunchKernelGGL((k_unpack_rows<uint32_t, U>), dim3(static_cast<unsigned>(rows * nchunks)),
+                           dim3(256), 0, stream, static_cast<const uint32_t *>(packed),
+                           static_cast<uint32_t *>(unpacked), unpacker, elems, P, W * L, nchunks);
+    } else {
+        const int64_t elems = row_bytes;
+        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
+        hipLaunchKernelGGL((k_unpack_rows<uint8_t, U>), dim3(static_cast<unsigned>(rows * nchunks)),
+                           dim3(256), 0, stream, static_cast<const uint8_t *>(packed),
+                           static_cast<uint8_t *>(unpacked), unpacker, elems, P, W * L, nchunks);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *pargmax,
+                         int B, int W, int L, int32_t *match_len, int32_t *best_beam,
+                         int32_t *accept_len, int32_t *accepted, hipStream_t stream) {
+    hipLaunchKernelGGL(k_accept, dim3(B), dim3(kWave), 0, stream, beams, unpacker, pargmax, W, L,
+                       match_len, best_beam, accept_len, accepted);
+    return hipGetLastError();
+}
+
+}  // namespace rd
