@@ -40,6 +40,8 @@ def parse():
                     help="rotate input sets until they exceed this many MB (defeats cache residency)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="requests in the oracle sample (0 = auto)")
+    ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
+                    help="also run a plain device copy of this size (a known-traffic reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -152,6 +154,20 @@ def main():
         rd.rd_unpack_accept(beams, pk["unpacker"], bufs.argmax, bufs.logits if full else None,
                             unpacked=bufs.unpacked, **bufs.accept)
         rec(5)
+
+    if args.copy_calibration_mb > 0:
+        # a device-to-device copy of known size; a 1 GB fill in between keeps
+        # the source out of the 256 MB last-level cache, so every byte is
+        # fetched from HBM
+        n = int(args.copy_calibration_mb * 1e6) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        flush = torch.empty(250_000_000, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            flush.fill_(1.0)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, flush
 
     for i in range(args.warmup):
         step(sets[i % n_sets])

@@ -211,16 +211,20 @@ __global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
     float lpart = 0.f;
 
     auto compute_tile = [&](int i, const Smem &sm) {
-        // S^T for 64 keys x this wave's 16 queries
+        // S^T for 64 keys x this wave's 16 queries.  Per head-dim step the
+        // four key blocks' fragments are read together and feed four
+        // independent accumulators, so LDS latency overlaps the MFMAs.
         f32x4 sc[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                const bf16x8 ka = as_bf16x8(ld16(&sm.k[(kb * 16 + lq) * Smem::KS + 32 * kc + 8 * kg]));
-                sc[kb] = mfma16x16x32(ka, qf[kc], sc[kb]);
-            }
+        for (int kc = 0; kc < NKC; ++kc) {
+            bf16x8 ka[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                ka[kb] = as_bf16x8(ld16(&sm.k[(kb * 16 + lq) * Smem::KS + 32 * kc + 8 * kg]));
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma16x16x32(ka[kb], qf[kc], sc[kb]);
         }
 
         // scale and mask; key of sc[kb][e] within the tile is kb*16 + 4*kg + e
@@ -283,14 +287,16 @@ __global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
                 pb[e] = static_cast<__bf16>(sc[2 * ks][e]);
                 pb[4 + e] = static_cast<__bf16>(sc[2 * ks + 1][e]);
             }
+            uint4 vv[NDB];
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const uint16_t *vrow = &sm.vt[(db * 16 + lq) * Smem::VS + 32 * ks + 4 * kg];
-                uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
-                uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                o[db] = mfma16x16x32(as_bf16x8(vv), pb, o[db]);
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
+                vv[db] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = mfma16x16x32(as_bf16x8(vv[db]), pb, o[db]);
         }
     };
 
@@ -483,10 +489,15 @@ AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int
     if (dtype != 1) return plan;  // fp32 path needs no workspace
     const int G = Hq / Hkv;
     plan.nqblk = (G * P_max + kBlockM - 1) / kBlockM;
+    // Split the cache only as far as needed for about four workgroups per
+    // CU, and never below 16 key tiles (1024 keys) per split: shorter
+    // splits spend more on partial writes and the merge than they gain in
+    // parallelism (measured on MI355X).
     const long units = static_cast<long>(B) * Hkv * plan.nqblk;
     const int tiles = (S_max + kBlockN - 1) / kBlockN;
     const long target = 4L * device_cu_count();
     int nsplit = static_cast<int>((target + units - 1) / units);
+    nsplit = min(nsplit, max(1, tiles / 16));
     nsplit = env_int("RD_ATTN_SPLITS", nsplit);
     nsplit = max(1, min(nsplit, min(max(tiles, 1), kMaxSplits)));
     const int chunk_tiles = (max(tiles, 1) + nsplit - 1) / nsplit;

@@ -53,9 +53,45 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
                                              static_cast<int>(bytes < kMaxRange ? bytes : kMaxRange), 0x00020000);
 }
 
+__device__ __forceinline__ bf16x8 as_bf16(const u32x4 &v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Explicitly scheduled stream loads.  The compiler inserts conservative
+// "wait for every outstanding load" points at loop back-edges, which would
+// drain a multi-stage prefetch ring once per trip.  Ring loads are therefore
+// issued with inline asm, invisible to the compiler's wait tracking, and the
+// consumer waits explicitly with stage_wait<N>(), N = number of ring loads
+// issued after the ones being waited for.  Loads complete in issue order, and
+// any other load the compiler adds in between only makes the wait stronger.
+// The wait statement takes the destination registers as in/out operands, so
+// no use of them can be scheduled before it.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t make_srsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes < kMaxRange ? bytes : kMaxRange));
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ void ring_load16(u32x4 &dst, const i32x4_t &rs, uint32_t off) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(rs));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <typename T>

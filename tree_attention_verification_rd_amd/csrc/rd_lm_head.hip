@@ -20,7 +20,6 @@
 // vocabulary range and writes one partial per (row, vocabulary tile); a
 // second kernel reduces the partials in a fixed order.
 #include <math.h>
-#include <stdlib.h>
 
 #include "rd_common.h"
 #include "rd_internal.h"
@@ -123,9 +122,9 @@ __global__ __launch_bounds__(256, MINB) void k_lm_head_bf16(LmArgs a) {
     const int nk_pad = (nk + NPF - 1) / NPF * NPF;
     const uint32_t rowb = static_cast<uint32_t>(K) * 2;
     const int wrows = max(0, min(a.V, vw0 + VW) - vw0);
-    const rsrc_t wres = make_rsrc(a.weight + static_cast<size_t>(min(vw0, a.V)) * K,
-                                  static_cast<uint32_t>(wrows) * rowb);
-    const rsrc_t xres = make_rsrc(a.hidden, static_cast<uint32_t>(static_cast<size_t>(a.B) * a.P * K * 2));
+    const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(vw0, a.V)) * K,
+                                    static_cast<uint32_t>(wrows) * rowb);
+    const i32x4_t xres = make_srsrc(a.hidden, static_cast<uint32_t>(static_cast<size_t>(a.B) * a.P * K * 2));
     uint32_t woff[NVB];
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) woff[vb] = (vb * 16 + lq) * rowb + 16 * kg;
@@ -137,36 +136,55 @@ __global__ __launch_bounds__(256, MINB) void k_lm_head_bf16(LmArgs a) {
         xoff[j] = (m < R) ? static_cast<uint32_t>(a.rowmap[m]) * rowb + 16 * (c % 8) : kOOB;
     }
 
-    // Each workgroup walks K from its own starting k-step (wrapping), so
-    // that concurrent workgroups do not all address the same offset within
+    // Each vocabulary tile walks K from its own starting k-step (wrapping),
+    // so that concurrent tiles do not all address the same offset within
     // their power-of-two-strided rows (which would crowd a few HBM
-    // channels).  Padding k-steps (kt >= nk) read zeros.
-    const int krot = (vt * 5 + rt * 3) % nk;
-    auto kstep = [&](int kt) { return kt < nk ? (kt + krot) % nk : nk; };
-    auto load_w = [&](uint4 (&dst)[NVB][2], int kt) {
-        const int kr = kstep(kt);
+    // channels).  The start depends on the vocabulary tile only: the row
+    // tiles that share these weight rows run side by side on one XCD and
+    // must walk K in the same order to share each chunk through L2.
+    // Stages are loaded in k order, so the rotated index is advanced
+    // incrementally; padding k-steps (kt >= nk) read zeros.
+    const int krot = (vt * 5) % nk;
+    int kload = 0;          // next k-step to load (unrotated)
+    int kload_rot = krot;   // its rotated index
+    auto next_kstep = [&]() {
+        const int kr = kload < nk ? kload_rot : nk;
+        ++kload;
+        kload_rot = (kload_rot + 1 == nk) ? 0 : kload_rot + 1;
+        return kr;
+    };
+    auto load_stage = [&](u32x4 (&w)[NVB][2], u32x4 (&x)[XLD]) {
+        const int kr = next_kstep();
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bool in = kr * kBK + 32 * ks + 8 * kg < K;
-                dst[vb][ks] = buf_load16(wres, in ? woff[vb] + (kr * kBK + 32 * ks) * 2 : kOOB);
+                ring_load16(w[vb][ks], wres, in ? woff[vb] + (kr * kBK + 32 * ks) * 2 : kOOB);
             }
-    };
-    auto load_x = [&](uint4 (&dst)[XLD], int kt) {
-        const int kr = kstep(kt);
 #pragma unroll
         for (int j = 0; j < XLD; ++j) {
             const int c = tid + 256 * j;
             const bool in = xoff[j] != kOOB && kr * kBK + 8 * (c % 8) < K;
-            dst[j] = buf_load16(xres, in ? xoff[j] + kr * kBK * 2 : kOOB);
+            ring_load16(x[j], xres, in ? xoff[j] + kr * kBK * 2 : kOOB);
         }
     };
-    auto store_x = [&](const uint4 (&src)[XLD], int buf) {
+    constexpr int kStageLoads = NVB * 2 + XLD;
+    // wait until stage `st` has landed: the NPF-1 younger stages stay in flight
+    auto stage_ready = [&](u32x4 (&w)[NVB][2], u32x4 (&x)[XLD]) {
+        vm_wait<(NPF - 1) * kStageLoads>();
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(w[vb][ks]));
+#pragma unroll
+        for (int j = 0; j < XLD; ++j) asm volatile("" : "+v"(x[j]));
+    };
+    auto store_x = [&](const u32x4 (&src)[XLD], int buf) {
 #pragma unroll
         for (int j = 0; j < XLD; ++j) {
             const int c = tid + 256 * j;
-            *reinterpret_cast<uint4 *>(&xs[buf][(c / 8) * XS + 8 * (c % 8)]) = src[j];
+            *reinterpret_cast<u32x4 *>(&xs[buf][(c / 8) * XS + 8 * (c % 8)]) = src[j];
         }
     };
 
@@ -181,35 +199,49 @@ __global__ __launch_bounds__(256, MINB) void k_lm_head_bf16(LmArgs a) {
     // complete in issue order, so the wait at k-step j only covers stage j
     // and the NPF-1 younger stages stay in flight.  X moves to LDS (double
     // buffered) right before its k-step; one barrier per k-step suffices.
-    uint4 wreg[NPF][NVB][2];
-    uint4 xreg[NPF][XLD];
+    u32x4 wreg[NPF][NVB][2];
+    u32x4 xreg[NPF][XLD];
 #pragma unroll
-    for (int st = 0; st < NPF; ++st) {
-        load_w(wreg[st], st);
-        load_x(xreg[st], st);
-    }
+    for (int st = 0; st < NPF; ++st) load_stage(wreg[st], xreg[st]);
 
     for (int kt0 = 0; kt0 < nk_pad; kt0 += NPF) {
 #pragma unroll
         for (int st = 0; st < NPF; ++st) {
             const int kt = kt0 + st;
             const int buf = st & 1;  // == kt & 1 since NPF is even
+            stage_ready(wreg[st], xreg[st]);
             store_x(xreg[st], buf);
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                // all X fragments of this half-step are read before the
+                // MFMAs that use them, so LDS latency overlaps the MFMAs
+                bf16x8 xb[NRB];
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    // branch-free: blocks past the valid rows multiply zeros
-                    const bf16x8 xb = as_bf16x8(ld16(&xs[buf][(rb * 16 + lq) * XS + 32 * ks + 8 * kg]));
+                for (int rb = 0; rb < NRB; ++rb)
+                    xb[rb] = as_bf16x8(ld16(&xs[buf][(rb * 16 + lq) * XS + 32 * ks + 8 * kg]));
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)  // blocks past the valid rows multiply zeros
 #pragma unroll
                     for (int vb = 0; vb < NVB; ++vb)
-                        acc[vb][rb] = mfma16x16x32(as_bf16x8(wreg[st][vb][ks]), xb, acc[vb][rb]);
-                }
+                        acc[vb][rb] = mfma16x16x32(as_bf16(wreg[st][vb][ks]), xb[rb], acc[vb][rb]);
             }
-            load_w(wreg[st], kt + NPF);
-            load_x(xreg[st], kt + NPF);
+            load_stage(wreg[st], xreg[st]);
         }
+    }
+
+    // The ring's trailing prefetches (past K) are still landing: wait for
+    // them with every slot tied, so that no register of an in-flight load
+    // is handed to other code before the data has arrived.
+    vm_wait<0>();
+#pragma unroll
+    for (int st = 0; st < NPF; ++st) {
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(wreg[st][vb][ks]));
+#pragma unroll
+        for (int j = 0; j < XLD; ++j) asm volatile("" : "+v"(xreg[st][j]));
     }
 
     // epilogue: acc[vb][rb][e] = logit(row r0 + rb*16 + lq, vocab vw0 + vb*16 + 4*kg + e)
@@ -356,21 +388,8 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const float *__restrict__
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// tile shapes: skinny (few rows) keeps all rows in one workgroup
-bool skinny(int B, int P) { return static_cast<long>(B) * P <= 512; }
-
-int lm_variant() {
-    const char *v = getenv("RD_LM_VARIANT");
-    return (v && *v) ? atoi(v) : 0;
-}
-
-int vocab_per_wg(int variant) {
-    switch (variant) {
-        case 3: case 4: return 4 * 16;
-        case 100: return 4 * 64;
-        default: return 4 * 32;
-    }
-}
+constexpr int kVocabPerWave = 32;
+constexpr int kRowTile = 128;
 
 }  // namespace
 
@@ -380,7 +399,7 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
     if (dtype == 0) {
         plan.vtile = 256;
     } else {
-        plan.vtile = vocab_per_wg(skinny(B, P_max) ? lm_variant() : 100);
+        plan.vtile = 4 * kVocabPerWave;
     }
     plan.nvt = (V + plan.vtile - 1) / plan.vtile;
     const size_t rows = static_cast<size_t>(plan.rows_pad);
@@ -417,19 +436,12 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.pval = pval;
         a.pidx = pidx;
         a.nvt = plan.nvt;
-        const int variant = skinny(B, P_max) ? lm_variant() : 100;
-        auto launch = [&](auto kern, int br) {
-            a.nrt = static_cast<int>((rows + br - 1) / br);
-            hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.nrt * a.nvt)), dim3(256), 0, stream, a);
-        };
-        switch (variant) {
-            case 1: launch(k_lm_head_bf16<32, 128, 4, 2>, 128); break;
-            case 2: launch(k_lm_head_bf16<32, 256, 2, 1>, 256); break;
-            case 3: launch(k_lm_head_bf16<16, 128, 4, 2>, 128); break;
-            case 4: launch(k_lm_head_bf16<16, 128, 2, 3>, 128); break;
-            case 100: launch(k_lm_head_bf16<64, 128, 2, 1>, 128); break;
-            default: launch(k_lm_head_bf16<32, 128, 2, 2>, 128); break;
-        }
+        // 4 wavefronts x 32 vocabulary rows, 128 compact rows per workgroup,
+        // two-stage load ring, two workgroups per CU: the best of the tile
+        // shapes measured on MI355X for both the few-row and many-row cases
+        a.nrt = static_cast<int>((rows + kRowTile - 1) / kRowTile);
+        hipLaunchKernelGGL((k_lm_head_bf16<kVocabPerWave, kRowTile, 2, 2>), dim3(static_cast<unsigned>(a.nrt * a.nvt)),
+                           dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
