@@ -64,15 +64,14 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Explicitly scheduled stream loads.  The compiler inserts conservative
-// "wait for every outstanding load" points at loop back-edges, which would
-// drain a multi-stage prefetch ring once per trip.  Ring loads are therefore
-// issued with inline asm, invisible to the compiler's wait tracking, and the
-// consumer waits explicitly with stage_wait<N>(), N = number of ring loads
-// issued after the ones being waited for.  Loads complete in issue order, and
-// any other load the compiler adds in between only makes the wait stronger.
-// The wait statement takes the destination registers as in/out operands, so
-// no use of them can be scheduled before it.
+// Explicitly counted loads.  The compiler inserts conservative "wait for
+// every outstanding load" points at loop back-edges and before any LDS read
+// that might alias a direct-to-LDS load, which would drain a multi-stage
+// prefetch ring once per trip.  Ring loads are therefore issued with inline
+// asm, invisible to the compiler's wait tracking, and the consumer waits
+// explicitly with vm_wait<N>(), N = number of ring loads issued after the
+// ones being waited for.  Loads complete in issue order, and any other load
+// the compiler adds in between only makes the wait stronger.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i32x4_t make_srsrc(const void *base, uint32_t bytes) {
@@ -85,13 +84,26 @@ __device__ __forceinline__ i32x4_t make_srsrc(const void *base, uint32_t bytes) 
     return r;
 }
 
-__device__ __forceinline__ void ring_load16(u32x4 &dst, const i32x4_t &rs, uint32_t off) {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(rs));
-}
-
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct global->LDS load (gfx950 buffer_load_dwordx4 ... lds): lane i's 16
+// bytes land at LDS byte address m0 + 16*i, with the wave-uniform m0 set just
+// before the load; an offset past the resource's range writes zeros.  No
+// register receives the data.  It is counted explicitly (see above): the
+// consumer waits with vm_wait<N>() and then a workgroup barrier before
+// reading the LDS it fills.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const i32x4_t &rs, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 ::"v"(off), "s"(rs), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (the low half of its flat address)
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 template <typename T>

@@ -34,6 +34,8 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
 struct LmPlan {
     int rows_pad;   // B * P_max
     int vtile;      // vocabulary columns per workgroup
+    int rtile;      // compact rows per workgroup (bf16)
+    int variant;    // bf16 tile shape
     int nvt;        // vocabulary tiles
     size_t ws_bytes;
 };

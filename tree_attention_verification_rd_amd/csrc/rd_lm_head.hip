@@ -7,19 +7,18 @@
 //
 // bf16 GEMM layout.  Only valid packed rows (p < packed_len[b]) are
 // computed: a small kernel compacts them into a row map.  The product is
-// formed transposed, C^T = W X^T, so that
-//   - the A operand is W: each wavefront streams its own vocabulary rows
-//     from HBM straight into registers (no LDS round trip -- no other
-//     wavefront needs them), kept NPF k-steps ahead in a register ring;
-//   - the B operand is X (hidden rows), shared by every wavefront of the
-//     workgroup and staged through double-buffered LDS;
-//   - each lane's accumulator holds four consecutive vocabulary entries of
-//     one row, which is what the argmax epilogue and the logits store want.
-// Per workgroup: 4 wavefronts x VW vocabulary rows, BR compact rows, K in
-// steps of 64.  The epilogue reduces (max, first index) over the tile's
-// vocabulary range and writes one partial per (row, vocabulary tile); a
-// second kernel reduces the partials in a fixed order.
+// formed transposed, C^T = W X^T (A operand = weight rows, B operand =
+// hidden rows), so each lane's accumulator holds four consecutive
+// vocabulary entries of one row -- what the argmax epilogue and the logits
+// store want.  Both operands are staged through LDS by direct global->LDS
+// loads (no registers, whole cache lines per instruction) into a ring of
+// k-steps of 64, and each of the four wavefronts multiplies a 128 x WR
+// block out of LDS with v_mfma_f32_16x16x32_bf16.  The epilogue reduces
+// (max, first index) over the tile's vocabulary range and writes one
+// partial per (row, vocabulary tile); a second kernel reduces the partials
+// in a fixed order.
 #include <math.h>
+#include <stdlib.h>
 
 #include "rd_common.h"
 #include "rd_internal.h"
@@ -78,231 +77,261 @@ __global__ __launch_bounds__(256) void k_rowmap(const int32_t *__restrict__ plen
     if (threadIdx.x == 0) *rcount = carry;
 }
 
-template <int VW, int BR, int NPF, int MINB>
-__global__ __launch_bounds__(256, MINB) void k_lm_head_bf16(LmArgs a) {
-    constexpr int NVB = VW / 16;
-    constexpr int NRB = BR / 16;
-    constexpr int XS = kBK + 8;          // LDS row stride (elements)
-    constexpr int XLD = BR * (kBK / 8) / 256;  // 16-byte pieces per thread per k-step
-    static_assert(NPF % 2 == 0, "the LDS buffer index must be static inside the unrolled ring");
-    __shared__ uint16_t xs[2][BR * XS];
-    __shared__ float redv[4][BR];
-    __shared__ int32_t redi[4][BR];
+template <int WV, int WR, int GV, int GR, int NS>
+__global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
+    static_assert(GV * GR == 4, "four wavefronts per workgroup");
+    static_assert(NS >= 2, "the ring needs a stage in flight while another is consumed");
+    static_assert(kBK == 64, "two 32-wide halves per k-step");
+    constexpr int BV = GV * WV;              // vocabulary rows per tile
+    constexpr int BR = GR * WR;              // compact hidden rows per tile
+    constexpr int NVB = WV / 16;
+    constexpr int NRB = WR / 16;
+    constexpr int kRowB = kBK * 2;           // bytes of one staged row (one cache line)
+    constexpr int kStageRows = BV + BR;
+    constexpr int kStageBytes = kStageRows * kRowB;
+    static_assert(kStageRows % 32 == 0, "whole 8-row loads, shared evenly by the wavefronts");
+    constexpr int NL = kStageRows / 32;      // LDS loads per wavefront per stage
+    constexpr int NLW = BV / 32;             // ... of weight rows
+    constexpr int NLX = BR / 32;             // ... of hidden rows
+    static_assert(BV % 32 == 0 && BR % 32 == 0, "each wavefront loads whole groups of both operands");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * kStageBytes];
 
     // wave-uniform values are read into scalar registers explicitly so the
     // buffer resources built from them stay scalar (no per-lane loops)
     const int R = __builtin_amdgcn_readfirstlane(*a.rcount);
-    const int ntiles = a.nrt * a.nvt;
-    const int t = xcd_tile(blockIdx.x, ntiles);
-    // groups of up to 8 row tiles walk the vocabulary together
-    constexpr int GM = 8;
-    const int grp = t / (GM * a.nvt);
-    const int gsz = min(GM, a.nrt - grp * GM);
-    const int within = t - grp * GM * a.nvt;
-    const int rt = grp * GM + within % gsz;
-    const int vt = within / gsz;
-    const int r0 = rt * BR;
-    if (r0 >= R) return;
-
+    const int nrt = (R + BR - 1) / BR;       // row tiles that hold valid rows
+    const int ntiles = nrt * a.nvt;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lq = lane & 15;
     const int kg = lane >> 4;
-    const int vw0 = vt * 4 * VW + wave * VW;
-    const int rvalid = min(BR, R - r0);
-    const int nrb = (rvalid + 15) / 16;
+    const int gv = wave % GV;
+    const int gr = wave / GV;
     const int K = a.K;
     const int nk = (K + kBK - 1) / kBK;
-
-    // Buffer loads: one resource over this wavefront's W rows (rows past V
-    // fall outside it) and one over all hidden rows.  Out-of-range rows and
-    // k-chunks get an out-of-range offset and read as zeros, so every
-    // thread issues the same loads on every path.
-    const int nk_pad = (nk + NPF - 1) / NPF * NPF;
     const uint32_t rowb = static_cast<uint32_t>(K) * 2;
-    const int wrows = max(0, min(a.V, vw0 + VW) - vw0);
-    const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(vw0, a.V)) * K,
-                                    static_cast<uint32_t>(wrows) * rowb);
+
+    // Staging.  A stage holds BV weight rows then BR hidden rows, kBK
+    // columns each, one 128-byte line per row.  Each load instruction moves
+    // 8 whole rows (coalesced cache lines); within a row the eight 16-byte
+    // chunks are stored XOR-swizzled by (row % 8), so the fragment reads
+    // below (16 rows x one chunk per instruction) hit distinct banks.  Lane
+    // i of a load covers staged row 8j + i/8 and stores LDS slot i%8, which
+    // holds chunk c = (i%8) ^ (i/8) of that row.  Load j = 4*i + wave is
+    // the wavefront's i-th: its first BV/32 loads are weight rows, the rest
+    // hidden rows.
+    const int lrow = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow;
     const i32x4_t xres = make_srsrc(a.hidden, static_cast<uint32_t>(static_cast<size_t>(a.B) * a.P * K * 2));
-    uint32_t woff[NVB];
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) woff[vb] = (vb * 16 + lq) * rowb + 16 * kg;
-    uint32_t xoff[XLD];
-#pragma unroll
-    for (int j = 0; j < XLD; ++j) {
-        const int c = tid + 256 * j;
-        const int m = r0 + c / 8;
-        xoff[j] = (m < R) ? static_cast<uint32_t>(a.rowmap[m]) * rowb + 16 * (c % 8) : kOOB;
-    }
+    const uint32_t lds0 = lds_addr_of(lds);
+    // fragment reads: lane reads row lq of each 16-row block, k-chunk
+    // 4*ks + kg, at its swizzled slot; the ks = 1 slot is the ks = 0 slot
+    // with chunk bit 2 flipped
+    const uint32_t sw = static_cast<uint32_t>((kg ^ (lq & 7)) << 4);
+    const uint32_t aoff = static_cast<uint32_t>(gv * WV + lq) * kRowB + sw;
+    const uint32_t boff = static_cast<uint32_t>(BV + gr * WR + lq) * kRowB + sw;
+    // All workgroups on one XCD (block i runs on XCD i % 8) walk K in the
+    // same order and mostly run side by side, so the rows they share are
+    // fetched into that XCD's L2 once; the XCDs start at different k-steps
+    // so that they do not all address the same offset of the power-of-two-
+    // strided rows at once (which would crowd a few HBM channels).
+    const int krot = ((blockIdx.x & 7) * nk / 8) % nk;
 
-    // Each vocabulary tile walks K from its own starting k-step (wrapping),
-    // so that concurrent tiles do not all address the same offset within
-    // their power-of-two-strided rows (which would crowd a few HBM
-    // channels).  The start depends on the vocabulary tile only: the row
-    // tiles that share these weight rows run side by side on one XCD and
-    // must walk K in the same order to share each chunk through L2.
-    // Stages are loaded in k order, so the rotated index is advanced
-    // incrementally; padding k-steps (kt >= nk) read zeros.
-    const int krot = (vt * 5) % nk;
-    int kload = 0;          // next k-step to load (unrotated)
-    int kload_rot = krot;   // its rotated index
-    auto next_kstep = [&]() {
-        const int kr = kload < nk ? kload_rot : nk;
-        ++kload;
-        kload_rot = (kload_rot + 1 == nk) ? 0 : kload_rot + 1;
-        return kr;
-    };
-    auto load_stage = [&](u32x4 (&w)[NVB][2], u32x4 (&x)[XLD]) {
-        const int kr = next_kstep();
+    // The grid is sized on the host for the largest possible row count, but
+    // only tiles with valid rows do work.  The first ntiles workgroups take
+    // them, XCD by XCD in contiguous ranges of the tile order (groups of up
+    // to GM row tiles walk the vocabulary together); the rest exit.  Since
+    // workgroups are dispatched in id order, the idle ones come last instead
+    // of interleaving with real ones (which would leave some shader engines
+    // with twice the work of others).
+    if (static_cast<int>(blockIdx.x) >= ntiles) return;
+    constexpr int GM = 8;
+    {
+        const int t = xcd_tile(blockIdx.x, ntiles);
+        const int grp = t / (GM * a.nvt);
+        const int gsz = min(GM, nrt - grp * GM);
+        const int within = t - grp * GM * a.nvt;
+        const int rt = grp * GM + within % gsz;
+        const int vt = within / gsz;
+        const int r0 = rt * BR;
+        const int v0 = vt * BV;
+
+        const int wrows = max(0, min(a.V - v0, BV));
+        const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(v0, a.V)) * K,
+                                        static_cast<uint32_t>(wrows) * rowb);
+        // weight rows past V fall outside wres; hidden rows past R get kOOB
+        const uint32_t wbase = static_cast<uint32_t>(8 * wave + lrow) * rowb + 16 * lchunk;
+        uint32_t xbase[NLX];
+#pragma unroll
+        for (int i = 0; i < NLX; ++i) {
+            const int m = r0 + 8 * (4 * (NLW + i) + wave) + lrow - BV;
+            xbase[i] = (m < R) ? static_cast<uint32_t>(a.rowmap[m]) * rowb + 16 * lchunk : kOOB;
+        }
+        // Stage kt (k-step (kt + krot) mod nk) goes to ring slot kt % NS.
+        // Stages past the last k-step still issue their loads, all out of
+        // range (zeros), so every wait below counts the same number of loads.
+        auto issue_stage = [&](int kt, int slot) {
+            const int kr = (kt < nk) ? ((kt + krot >= nk) ? kt + krot - nk : kt + krot) : -1;
+            const bool kin = kr >= 0 && kr * kBK + 8 * lchunk < K;
+            const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
+            const uint32_t sbase = lds0 + slot * kStageBytes + wave * 1024;
+#pragma unroll
+            for (int i = 0; i < NLW; ++i)
+                lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 32 * rowb + kadd : kOOB);
+#pragma unroll
+            for (int i = 0; i < NLX; ++i)
+                lds_dma16(sbase + (NLW + i) * 4096, xres, kin ? xbase[i] + kadd : kOOB);
+        };
+        // a wavefront whose rows are all padding only helps with the loads
+        const bool active = r0 + gr * WR < R;
+
+        f32x4 acc[NVB][NRB];
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bool in = kr * kBK + 32 * ks + 8 * kg < K;
-                ring_load16(w[vb][ks], wres, in ? woff[vb] + (kr * kBK + 32 * ks) * 2 : kOOB);
-            }
-#pragma unroll
-        for (int j = 0; j < XLD; ++j) {
-            const int c = tid + 256 * j;
-            const bool in = xoff[j] != kOOB && kr * kBK + 8 * (c % 8) < K;
-            ring_load16(x[j], xres, in ? xoff[j] + kr * kBK * 2 : kOOB);
-        }
-    };
-    constexpr int kStageLoads = NVB * 2 + XLD;
-    // wait until stage `st` has landed: the NPF-1 younger stages stay in flight
-    auto stage_ready = [&](u32x4 (&w)[NVB][2], u32x4 (&x)[XLD]) {
-        vm_wait<(NPF - 1) * kStageLoads>();
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(w[vb][ks]));
-#pragma unroll
-        for (int j = 0; j < XLD; ++j) asm volatile("" : "+v"(x[j]));
-    };
-    auto store_x = [&](const u32x4 (&src)[XLD], int buf) {
-#pragma unroll
-        for (int j = 0; j < XLD; ++j) {
-            const int c = tid + 256 * j;
-            *reinterpret_cast<u32x4 *>(&xs[buf][(c / 8) * XS + 8 * (c % 8)]) = src[j];
-        }
-    };
+            for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    f32x4 acc[NVB][NRB];
+        // Ring of NS LDS stages.  Stages 0..NS-2 are issued up front.  At
+        // the top of k-step kt this wavefront's loads of stage kt have landed
+        // once at most (NS-2)*NL of its loads remain outstanding; the barrier
+        // then publishes every wavefront's share and also certifies that all
+        // reads of slot (kt-1) % NS are done, so stage kt+NS-1 may be loaded
+        // into it.
+        //
+        // Fragments are software-pipelined across the barrier: the second
+        // half (k 32..63) of k-step kt is read into registers before the
+        // barrier of k-step kt+1 and multiplied after it, while the
+        // first-half reads of k-step kt+1 are in flight, so LDS latency does
+        // not stall the MFMAs.  (The first k-step multiplies zero fragments
+        // in that slot.)
+        auto read_frags = [&](const uint8_t *st, uint32_t x, bf16x8 (&fa)[NVB], bf16x8 (&fb)[NRB]) {
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb)
+            for (int vb = 0; vb < NVB; ++vb)
+                fa[vb] = *reinterpret_cast<const bf16x8 *>(st + ((aoff ^ x) + vb * 16 * kRowB));
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < NRB; ++rb)
+                fb[rb] = *reinterpret_cast<const bf16x8 *>(st + ((boff ^ x) + rb * 16 * kRowB));
+        };
+        auto mma = [&](const bf16x8 (&fa)[NVB], const bf16x8 (&fb)[NRB]) {
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = mfma16x16x32(fa[vb], fb[rb], acc[vb][rb]);
+        };
+        bf16x8 ha[NVB], hb[NRB];  // second half of the previous k-step
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) ha[vb] = bf16x8{};
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) hb[rb] = bf16x8{};
 
-    // Stage ring: the W and X loads of k-step j are issued together, NPF
-    // k-steps before j is computed, into register slot j % NPF.  Loads
-    // complete in issue order, so the wait at k-step j only covers stage j
-    // and the NPF-1 younger stages stay in flight.  X moves to LDS (double
-    // buffered) right before its k-step; one barrier per k-step suffices.
-    u32x4 wreg[NPF][NVB][2];
-    u32x4 xreg[NPF][XLD];
 #pragma unroll
-    for (int st = 0; st < NPF; ++st) load_stage(wreg[st], xreg[st]);
+        for (int s = 0; s < NS - 1; ++s) issue_stage(s, s);
 
-    for (int kt0 = 0; kt0 < nk_pad; kt0 += NPF) {
+        for (int kt0 = 0; kt0 < nk; kt0 += NS) {
 #pragma unroll
-        for (int st = 0; st < NPF; ++st) {
-            const int kt = kt0 + st;
-            const int buf = st & 1;  // == kt & 1 since NPF is even
-            stage_ready(wreg[st], xreg[st]);
-            store_x(xreg[st], buf);
-            __syncthreads();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                // all X fragments of this half-step are read before the
-                // MFMAs that use them, so LDS latency overlaps the MFMAs
-                bf16x8 xb[NRB];
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
-                    xb[rb] = as_bf16x8(ld16(&xs[buf][(rb * 16 + lq) * XS + 32 * ks + 8 * kg]));
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)  // blocks past the valid rows multiply zeros
-#pragma unroll
-                    for (int vb = 0; vb < NVB; ++vb)
-                        acc[vb][rb] = mfma16x16x32(as_bf16(wreg[st][vb][ks]), xb[rb], acc[vb][rb]);
-            }
-            load_stage(wreg[st], xreg[st]);
-        }
-    }
-
-    // The ring's trailing prefetches (past K) are still landing: wait for
-    // them with every slot tied, so that no register of an in-flight load
-    // is handed to other code before the data has arrived.
-    vm_wait<0>();
-#pragma unroll
-    for (int st = 0; st < NPF; ++st) {
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(wreg[st][vb][ks]));
-#pragma unroll
-        for (int j = 0; j < XLD; ++j) asm volatile("" : "+v"(xreg[st][j]));
-    }
-
-    // epilogue: acc[vb][rb][e] = logit(row r0 + rb*16 + lq, vocab vw0 + vb*16 + 4*kg + e)
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        if (rb < nrb) {
-            const int m = r0 + rb * 16 + lq;
-            const bool mvalid = m < R;
-            const int pr = mvalid ? a.rowmap[m] : 0;
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) {
-                const int v = vw0 + vb * 16 + 4 * kg;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (v + e < a.V && better(acc[vb][rb][e], v + e, bv, bi)) {
-                        bv = acc[vb][rb][e];
-                        bi = v + e;
-                    }
-                if (a.logits && mvalid) {
-                    uint16_t *dst = a.logits + static_cast<size_t>(pr) * a.V + v;
-                    if (v + 3 < a.V && (a.V % 4 == 0)) {
-                        u16x4 w = {f32_to_bf16_bits(acc[vb][rb][0]), f32_to_bf16_bits(acc[vb][rb][1]),
-                                   f32_to_bf16_bits(acc[vb][rb][2]), f32_to_bf16_bits(acc[vb][rb][3])};
-                        *reinterpret_cast<u16x4 *>(dst) = w;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v + e < a.V) dst[e] = f32_to_bf16_bits(acc[vb][rb][e]);
-                    }
+            for (int s = 0; s < NS; ++s) {
+                const int kt = kt0 + s;
+                if (kt >= nk) break;
+                vm_wait<(NS - 2) * NL>();
+                __syncthreads();
+                issue_stage(kt + NS - 1, (s + NS - 1) % NS);
+                if (active) {
+                    const uint8_t *st = lds + s * kStageBytes;
+                    bf16x8 fa[NVB], fb[NRB];
+                    read_frags(st, 0u, fa, fb);
+                    mma(ha, hb);
+                    read_frags(st, 64u, ha, hb);
+                    mma(fa, fb);
+                    // keep that order: reads, multiplies, reads, multiplies
+                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
                 }
             }
         }
+        if (active) mma(ha, hb);
+        vm_wait<0>();
+        __syncthreads();  // the padding stages' loads have landed before LDS is reused
+
+        // epilogue: acc[vb][rb][e] = logit(row r0 + gr*WR + rb*16 + lq,
+        //                                   vocab v0 + gv*WV + vb*16 + 4*kg + e)
+        float *redv = reinterpret_cast<float *>(lds);
+        int32_t *redi = reinterpret_cast<int32_t *>(lds + GV * BR * 4);
 #pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float ov = shfl_xor(bv, off);
-            const int oi = shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int row = gr * WR + rb * 16 + lq;
+            const int m = r0 + row;
+            const bool mvalid = m < R;
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            if (active) {
+                const int pr = mvalid ? a.rowmap[m] : 0;
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const int v = v0 + gv * WV + vb * 16 + 4 * kg;
+                    // candidates come in increasing vocabulary order, so a
+                    // strict compare keeps the first of equal values
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool take = (v + e < a.V) & (acc[vb][rb][e] > bv);
+                        bv = take ? acc[vb][rb][e] : bv;
+                        bi = take ? v + e : bi;
+                    }
+                    if (a.logits && mvalid) {
+                        uint16_t *dst = a.logits + static_cast<size_t>(pr) * a.V + v;
+                        if (v + 3 < a.V && (a.V % 4 == 0)) {
+                            u16x4 w = {f32_to_bf16_bits(acc[vb][rb][0]), f32_to_bf16_bits(acc[vb][rb][1]),
+                                       f32_to_bf16_bits(acc[vb][rb][2]), f32_to_bf16_bits(acc[vb][rb][3])};
+                            *reinterpret_cast<u16x4 *>(dst) = w;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (v + e < a.V) dst[e] = f32_to_bf16_bits(acc[vb][rb][e]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ov = shfl_xor(bv, off);
+                const int oi = shfl_xor(bi, off);
+                if (better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (kg == 0) {
+                if (GV == 1) {
+                    if (mvalid) {
+                        const size_t pr = static_cast<size_t>(a.rowmap[m]);
+                        a.pval[pr * a.nvt + vt] = bv;
+                        a.pidx[pr * a.nvt + vt] = bi;
+                    }
+                } else {
+                    redv[gv * BR + row] = bv;
+                    redi[gv * BR + row] = bi;
+                }
             }
         }
-        if (kg == 0) {
-            redv[wave][rb * 16 + lq] = bv;
-            redi[wave][rb * 16 + lq] = bi;
-        }
-    }
-    __syncthreads();
-    for (int i = tid; i < rvalid; i += 256) {
-        float bv = redv[0][i];
-        int bi = redi[0][i];
+        if (GV > 1) {
+            __syncthreads();
+            const int rvalid = min(BR, R - r0);
+            for (int i = tid; i < rvalid; i += 256) {
+                float bv = redv[i];
+                int bi = redi[i];
 #pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(redv[w][i], redi[w][i], bv, bi)) {
-                bv = redv[w][i];
-                bi = redi[w][i];
+                for (int g = 1; g < GV; ++g)
+                    if (better(redv[g * BR + i], redi[g * BR + i], bv, bi)) {
+                        bv = redv[g * BR + i];
+                        bi = redi[g * BR + i];
+                    }
+                const size_t pr = static_cast<size_t>(a.rowmap[r0 + i]);
+                a.pval[pr * a.nvt + vt] = bv;
+                a.pidx[pr * a.nvt + vt] = bi;
             }
-        const size_t pr = static_cast<size_t>(a.rowmap[r0 + i]);
-        a.pval[pr * a.nvt + vt] = bv;
-        a.pidx[pr * a.nvt + vt] = bi;
+        }
     }
 }
 
@@ -388,9 +417,6 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const float *__restrict__
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-constexpr int kVocabPerWave = 32;
-constexpr int kRowTile = 128;
-
 }  // namespace
 
 LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
@@ -398,8 +424,18 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
     plan.rows_pad = B * P_max;
     if (dtype == 0) {
         plan.vtile = 256;
+        plan.rtile = 1;
+        plan.variant = 0;
     } else {
-        plan.vtile = 4 * kVocabPerWave;
+        // Two tile shapes.  Few rows (the weight stream dominates): 128
+        // vocabulary x 256 rows per tile, 128x64 per wavefront, three-stage
+        // ring -- twice as many tiles to spread over the CUs.  Many rows (the
+        // MFMAs dominate): 256 x 256 per tile, 128x128 per wavefront, two
+        // stages -- a third less L2 traffic per flop.  RD_LM_VARIANT forces one.
+        const char *env = getenv("RD_LM_VARIANT");
+        plan.variant = (env && *env) ? (atoi(env) != 0) : (plan.rows_pad > 512 ? 1 : 0);
+        plan.vtile = plan.variant ? 256 : 128;
+        plan.rtile = 256;
     }
     plan.nvt = (V + plan.vtile - 1) / plan.vtile;
     const size_t rows = static_cast<size_t>(plan.rows_pad);
@@ -436,12 +472,12 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.pval = pval;
         a.pidx = pidx;
         a.nvt = plan.nvt;
-        // 4 wavefronts x 32 vocabulary rows, 128 compact rows per workgroup,
-        // two-stage load ring, two workgroups per CU: the best of the tile
-        // shapes measured on MI355X for both the few-row and many-row cases
-        a.nrt = static_cast<int>((rows + kRowTile - 1) / kRowTile);
-        hipLaunchKernelGGL((k_lm_head_bf16<kVocabPerWave, kRowTile, 2, 2>), dim3(static_cast<unsigned>(a.nrt * a.nvt)),
-                           dim3(256), 0, stream, a);
+        a.nrt = static_cast<int>((rows + plan.rtile - 1) / plan.rtile);
+        const dim3 grid(static_cast<unsigned>(a.nrt * a.nvt));
+        if (plan.variant == 0)
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
