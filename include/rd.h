@@ -135,7 +135,7 @@ size_t rd_tree_attention_workspace_size(int dtype, int B, int P_max, int Hq, int
  *   k_cache, v_cache (dev) [B,Hkv,S_max,D]
  *   kv_len  (dev) [B]  cached tokens of request b, 0 <= kv_len[b] <= S_max
  *   mask, packed_len (dev) from rd_tree_mask / rd_pack_beams
- *   scale   softmax scale; 0 selects 1/sqrt(D)
+ *   scale   softmax scale, finite and >= 0; 0 selects 1/sqrt(D)
  *   out     (dev) [B,P_max,Hq,D]  rows at or past packed_len are written as 0
  *   ws      (dev) workspace of ws_bytes >= rd_tree_attention_workspace_size()
  * Limits: D in {64,128}, Hq % Hkv == 0, P_max <= RD_MAX_BEAMS*RD_MAX_BEAM_LEN.

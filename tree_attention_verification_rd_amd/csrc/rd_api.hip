@@ -99,7 +99,7 @@ int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v
     if (B == 0 || P_max == 0 || Hq == 0) return RD_OK;
     if (!q || !k_new || !v_new || !kv_len || !mask || !packed_len || !out) return RD_E_ARG;
     if (S_max > 0 && (!k_cache || !v_cache)) return RD_E_ARG;
-    if (!(scale >= 0.f) || scale != scale) return RD_E_ARG;
+    if (!(scale >= 0.f) || !(scale <= 3.4e38f)) return RD_E_ARG;  // finite, non-negative (rejects NaN)
     const rd::AttnPlan plan = rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, S_max);
     if (ws_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && !ws)) return RD_E_WORKSPACE;
     return hip_status(rd::launch_attention(dtype, plan, q, k_new, v_new, k_cache, v_cache, kv_len, mask, packed_len,

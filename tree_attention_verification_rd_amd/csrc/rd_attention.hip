@@ -7,21 +7,27 @@
 // (SpecInfer's topology-aware causal mask, speculative-decoding survey,
 // "Token Tree Verifier").
 //
-// bf16 kernel layout.  One workgroup (4 wavefronts) handles 64 query rows of
-// one (request, KV head) and one split of the KV cache; row r of the
+// bf16 kernel layout.  One workgroup (4 wavefronts) handles up to RB query
+// rows of one (request, KV head) and one split of the KV cache; row r of the
 // (request, KV head) is packed token r / G, query head g*G + r % G, so the G
-// heads sharing a KV head share every K/V tile.  Keys stream through LDS in
-// tiles of 64: cache tiles first, then (last split only) the packed tiles up
-// to the largest token of the block -- parents precede children, so later
-// tokens cannot be ancestors.
+// heads sharing a KV head share every K/V tile, and all rows of a (request,
+// KV head) normally sit in one workgroup, so the cache is streamed once.
+// Keys stream through LDS in tiles of 64: cache tiles first, then (last
+// split only) the packed tiles up to the largest token of the block --
+// parents precede children, so later tokens cannot be ancestors.
 //
-// Each wavefront owns 16 query rows.  Scores are computed transposed,
-// S^T = K Q^T (A = K rows from LDS, B = Q held in registers), so each lane's
+// K and V tiles are copied global->LDS by direct loads (whole cache lines,
+// no registers) into a ring of NS stages, in their natural [key][d] layout
+// with 16-byte chunks XOR-swizzled by key.  Scores are computed transposed,
+// S^T = K Q^T (A = K rows, B = Q held in registers), so each lane's
 // accumulator column is one query and the probabilities P^T come out of the
-// MFMA already in the B-operand layout of O^T = V^T P^T; only V is
-// transposed, once, when a tile is written to LDS.  Online softmax runs in
-// fp32 in the log2 domain.  With more than one split, each split writes
-// (max, sum, unnormalised O) in fp32 and a combine kernel merges them.
+// MFMA already in the B-operand layout of O^T = V^T P^T.  The V^T operand
+// is read with the gfx950 LDS transpose load (ds_read_b64_tr_b16), which
+// turns a 16-lane group's 16 x 4 block into 4 consecutive keys per lane.
+// Each wavefront owns up to QPW blocks of 16 query rows and reuses every
+// K and V fragment it reads across them.  Online softmax runs in fp32 in
+// the log2 domain.  With more than one split, each split writes (max, sum,
+// unnormalised O) in fp32 and a combine kernel merges them.
 #include <math.h>
 #include <stdlib.h>
 
@@ -32,10 +38,12 @@ namespace rd {
 
 namespace {
 
-constexpr int kBlockM = 64;  // query rows per workgroup
 constexpr int kBlockN = 64;  // keys per tile
+constexpr int kCombRows = 64;  // rows per combine workgroup
 constexpr int kMaxSplits = 64;
 constexpr int kMaxMaskWords = (kMaxBeams * kMaxBeamLen) / 32;
+constexpr int kStages = 3;
+constexpr float kRescale = 8.f;  // lazy-rescale threshold of the online softmax (log2 units)
 
 struct AttnArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
@@ -44,18 +52,10 @@ struct AttnArgs {
     const int32_t *plen;
     int B, P, Hq, Hkv, G, S_max, nw;
     float scale_log2;
-    int nqblk, nsplit, chunk;
+    int nqblk, nsplit, chunk, rows_unit;  // rows_unit = nqblk * rows per workgroup
     uint16_t *out;
-    float *ws_o;    // [B, Hkv, nsplit, nqblk*64, D]
-    float2 *ws_ml;  // [B, Hkv, nsplit, nqblk*64]
-};
-
-template <int D>
-struct AttnSmem {
-    static constexpr int KS = D + 8;        // K row stride (elements)
-    static constexpr int VS = kBlockN + 8;  // V^T row stride (elements)
-    uint16_t k[kBlockN * KS];
-    uint16_t vt[D * VS];
+    float *ws_o;    // [B, Hkv, nsplit, rows_unit, D]
+    float2 *ws_ml;  // [B, Hkv, nsplit, rows_unit]
 };
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -66,27 +66,43 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
-    constexpr int NKC = D / 32;          // k-steps over the head dim (QK^T)
-    constexpr int NDB = D / 16;          // 16-row blocks of the head dim (PV)
-    constexpr int KCH = D / 8;           // 16-byte chunks per key row
-    constexpr int KLD = kBlockN * KCH / 256;  // K chunks per thread per tile
-    using Smem = AttnSmem<D>;
-    __shared__ Smem smem[2];
-    __shared__ uint32_t mwords[kBlockM * kMaxMaskWords];  // tree-mask rows of this block's tokens
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-    const int ntiles = a.B * a.Hkv * a.nsplit * a.nqblk;
-    const int t = xcd_tile(blockIdx.x, ntiles);
-    const int qb = t % a.nqblk;
-    int rest = t / a.nqblk;
+// LDS transpose load: within each 16-lane group, lane i receives element
+// i % 4 of the 4-element rows addressed by lanes i/4, i/4 + 4, i/4 + 8 and
+// i/4 + 12 (lane layout established on gfx950).
+__device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4 *>(static_cast<uintptr_t>(addr)));
+}
+
+template <int D, int QPW, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
+    constexpr int NKC = D / 32;              // k-steps over the head dim (QK^T)
+    constexpr int NDB = D / 16;              // 16-row blocks of the head dim (PV)
+    constexpr int KCH = D / 8;               // 16-byte chunks per key row
+    constexpr int ROWB = D * 2;              // bytes per key row
+    constexpr int TILEB = kBlockN * ROWB;    // bytes of one K or V tile
+    constexpr int STAGEB = 2 * TILEB;        // K tile then V tile
+    constexpr int KPL = 1024 / ROWB;         // keys per 1 KB load instruction
+    constexpr int NT = 64 * NWAVE;           // threads per workgroup
+    constexpr int NLD = kBlockN / KPL / NWAVE;  // load instructions per wavefront per operand per tile
+    constexpr int RB = NWAVE * QPW * 16;     // query rows per workgroup
+    static_assert(NLD >= 1, "every wavefront issues loads");
+    static_assert(KCH >= 8, "the swizzle permutes 8 chunks");
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[kStages * STAGEB];
+    __shared__ uint32_t mwords[RB * kMaxMaskWords];  // tree-mask rows of this block's tokens
+
+    // row blocks are the slowest index: blocks with no valid rows (their
+    // count depends on the packed lengths) come last in dispatch order
+    const int L = a.B * a.Hkv * a.nsplit;
+    const int qb = blockIdx.x / L;
+    const int rest = blockIdx.x - qb * L;
     const int s = rest % a.nsplit;
-    rest /= a.nsplit;
-    const int g = rest % a.Hkv;
-    const int b = rest / a.Hkv;
+    const int g = (rest / a.nsplit) % a.Hkv;
+    const int b = rest / (a.nsplit * a.Hkv);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lq = lane & 15;
     const int kg = lane >> 4;
@@ -95,13 +111,13 @@ __global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
     const int kvl = min(max(a.kv_len[b], 0), a.S_max);
     const int Mb = a.G * Pb;
     const int Mpad = a.G * a.P;
-    const int row0 = qb * kBlockM;
+    const int row0 = qb * RB;
 
     if (row0 >= Mb) {
         // no valid query rows: with a single split this block owns the
         // padding rows of the output and writes them as zeros
         if (a.nsplit == 1) {
-            for (int i = tid; i < kBlockM * KCH; i += 256) {
+            for (int i = tid; i < RB * KCH; i += NT) {
                 const int r = row0 + i / KCH;
                 if (r >= Mpad) continue;
                 const int pz = r / a.G, hz = g * a.G + r % a.G;
@@ -117,232 +133,297 @@ __global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
     const int ncache = (c1 > c0) ? (c1 - c0 + kBlockN - 1) / kBlockN : 0;
     int tok_hi = 0, npk = 0;
     if (s == a.nsplit - 1) {
-        tok_hi = (min(row0 + kBlockM, Mb) - 1) / a.G + 1;
+        tok_hi = (min(row0 + RB, Mb) - 1) / a.G + 1;
         npk = (tok_hi + kBlockN - 1) / kBlockN;
     }
     const int ntile = ncache + npk;
+    const int tok_lo = row0 / a.G;
 
-    // this lane's query row
-    const int r = row0 + wave * 16 + lq;
-    const bool rvalid = r < Mb;
-    const int p = rvalid ? r / a.G : 0;
-    const int h = g * a.G + (rvalid ? r % a.G : 0);
-    bf16x8 qf[NKC];
-    {
+    // this lane's query rows: block qi of wavefront w covers rows
+    // row0 + (NWAVE*qi + w)*16 .. +15 (interleaved, so few rows still
+    // spread over the wavefronts)
+    // A wavefront with at least one valid row multiplies all its blocks
+    // (padding rows hold zero queries); one with none only helps with the
+    // loads.  Valid rows form a prefix, so block 0 decides.
+    bf16x8 qf[QPW][NKC];
+    int lt[QPW];  // token of the row relative to tok_lo
+    const bool wave_active = row0 + wave * 16 < Mb;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+        const int r = row0 + (NWAVE * qi + wave) * 16 + lq;
+        const bool rvalid = r < Mb;
+        const int p = rvalid ? r / a.G : 0;
+        const int h = g * a.G + (rvalid ? r % a.G : 0);
+        lt[qi] = rvalid ? p - tok_lo : 0;
         const uint16_t *qrow = a.q + ((static_cast<size_t>(b) * a.P + p) * a.Hq + h) * D;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
-            qf[kc] = as_bf16x8(rvalid ? ld16(qrow + 32 * kc + 8 * kg) : make_uint4(0, 0, 0, 0));
+            qf[qi][kc] = as_bf16x8(rvalid ? ld16(qrow + 32 * kc + 8 * kg) : make_uint4(0, 0, 0, 0));
     }
     // tokens of this block and their tree-mask rows, staged in LDS once
-    const int tok_lo = row0 / a.G;
     if (npk > 0) {
         const int ntok = tok_hi - tok_lo;
         const uint32_t *msrc = a.mask + (static_cast<size_t>(b) * a.P + tok_lo) * a.nw;
-        for (int i = tid; i < ntok * a.nw; i += 256) mwords[i] = msrc[i];
+        for (int i = tid; i < ntok * a.nw; i += NT) mwords[i] = msrc[i];
     }
-    const int lt = rvalid ? p - tok_lo : 0;
+    // The Q loads must land before the ring starts: at a first use inside
+    // the loop the compiler would wait for them -- and thereby for every ring
+    // load issued after them.
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[qi][kc]));
 
     // K/V rows of tile i: cache tiles come first, then the packed tiles.
-    // Buffer loads with one resource per source: keys past the valid range
-    // get an out-of-range offset and read as zeros, so every thread issues
-    // the same loads on every path and no select is needed.
+    // Keys past the valid range get an out-of-range offset and load zeros.
     const size_t cache_base = (static_cast<size_t>(b) * a.Hkv + g) * a.S_max * D;
     const size_t fresh_base = (static_cast<size_t>(b) * a.P * a.Hkv + g) * D;
     const uint32_t cache_bytes = static_cast<uint32_t>(min<size_t>(static_cast<size_t>(a.S_max) * D * 2, kMaxRange));
     const uint32_t fresh_bytes = static_cast<uint32_t>(min<size_t>(static_cast<size_t>(a.P) * a.Hkv * D * 2, kMaxRange));
-    const rsrc_t rk_c = make_rsrc(a.k_cache + cache_base, cache_bytes);
-    const rsrc_t rv_c = make_rsrc(a.v_cache + cache_base, cache_bytes);
-    const rsrc_t rk_n = make_rsrc(a.k_new + fresh_base, fresh_bytes);
-    const rsrc_t rv_n = make_rsrc(a.v_new + fresh_base, fresh_bytes);
-
-    // V loader threads: 16 key quads x KCH head-dim chunks (all 256 threads
-    // for D = 128); the others repeat a load and skip the store
-    const bool vthread = tid < 16 * KCH;
-    const int vkq = tid & 15;                   // key quad: keys 4*vkq .. 4*vkq+3
-    const int vdc = vthread ? (tid >> 4) : 0;   // head-dim chunk: d = 8*vdc .. 8*vdc+7
+    const i32x4_t rk_c = make_srsrc(a.k_cache + cache_base, cache_bytes);
+    const i32x4_t rv_c = make_srsrc(a.v_cache + cache_base, cache_bytes);
+    const i32x4_t rk_n = make_srsrc(a.k_new + fresh_base, fresh_bytes);
+    const i32x4_t rv_n = make_srsrc(a.v_new + fresh_base, fresh_bytes);
+    const uint32_t lds0 = lds_addr_of(stage);
 
     // Cache tiles are visited from a per-block starting tile (wrapping) so
     // that concurrent blocks, whose slabs sit at power-of-two strides, do
     // not all address the same offsets and crowd a few HBM channels.
     const int trot = ncache > 0 ? (b * 7 + g * 3 + qb * 5) % ncache : 0;
-    auto load_tile = [&](uint4 (&kr)[KLD], uint4 (&vr)[4], int i) {
+    // Load j = NWAVE*jj + wave of an operand covers tile keys KPL*j .. +KPL-1;
+    // lane i stores LDS chunk slot i % KCH of key KPL*j + i / KCH, which
+    // holds head-dim chunk slot ^ (key & 7).
+    const int lkey = lane / KCH;
+    const int lslot = lane % KCH;
+    auto issue_tile = [&](int i, int slot) {
         const bool cache = i < ncache;
-        const rsrc_t rk = cache ? rk_c : rk_n;
-        const rsrc_t rv = cache ? rv_c : rv_n;
-        const int ic = cache ? (i + trot) % ncache : 0;
+        const i32x4_t rk = cache ? rk_c : rk_n;
+        const i32x4_t rv = cache ? rv_c : rv_n;
+        const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
         const int kbase = cache ? c0 + ic * kBlockN : (i - ncache) * kBlockN;
-        const int klim = cache ? c1 : tok_hi;
-        const uint32_t rowb = cache ? D * 2 : static_cast<uint32_t>(a.Hkv) * D * 2;
+        const int klim = (i >= ntile) ? 0 : (cache ? c1 : tok_hi);
+        const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
+        const uint32_t kdst = lds0 + slot * STAGEB;
 #pragma unroll
-        for (int j = 0; j < KLD; ++j) {
-            const int c = tid + 256 * j;
-            const int key = kbase + c / KCH;
-            kr[j] = buf_load16(rk, key < klim ? key * rowb + (c % KCH) * 16 : kOOB);
-        }
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int key = kbase + 4 * vkq + r4;
-            vr[r4] = buf_load16(rv, key < klim ? key * rowb + vdc * 16 : kOOB);
-        }
-    };
-    auto store_tile = [&](const uint4 (&kr)[KLD], const uint4 (&vr)[4], Smem &sm) {
-#pragma unroll
-        for (int j = 0; j < KLD; ++j) {
-            const int c = tid + 256 * j;
-            *reinterpret_cast<uint4 *>(&sm.k[(c / KCH) * Smem::KS + 8 * (c % KCH)]) = kr[j];
-        }
-        if (vthread) {
-            u16x8 v[4];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) __builtin_memcpy(&v[r4], &vr[r4], 16);
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                u16x4 col = {v[0][jj], v[1][jj], v[2][jj], v[3][jj]};
-                *reinterpret_cast<u16x4 *>(&sm.vt[(8 * vdc + jj) * Smem::VS + 4 * vkq]) = col;
-            }
+        for (int jj = 0; jj < NLD; ++jj) {
+            const int j = NWAVE * jj + wave;
+            const int kl = KPL * j + lkey;
+            const int key = kbase + kl;
+            const uint32_t off = key < klim ? static_cast<uint32_t>(key) * rowstride + ((lslot ^ (kl & 7)) << 4) : kOOB;
+            lds_dma16(kdst + j * 1024, rk, off);
+            lds_dma16(kdst + TILEB + j * 1024, rv, off);
         }
     };
 
-    f32x4 o[NDB];
+    // fragment offsets within a stage (see the swizzle above)
+    uint32_t koff[NKC];  // K row (kb*16 + lq), chunk 4*kc + kg; add kb*16*ROWB
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mrun = kNegBig;
-    float lpart = 0.f;
-
-    auto compute_tile = [&](int i, const Smem &sm) {
-        // S^T for 64 keys x this wave's 16 queries.  Per head-dim step the
-        // four key blocks' fragments are read together and feed four
-        // independent accumulators, so LDS latency overlaps the MFMAs.
-        f32x4 sc[4];
+    for (int kc = 0; kc < NKC; ++kc) koff[kc] = lq * ROWB + (((4 * kc + kg) ^ (lq & 7)) << 4);
+    // V^T: 16-lane group kg reads keys base + 4*kg + j/4 (j = lane % 16),
+    // head dims 16*db + 4*(j%4) .. +3; chunk 2*db + (j%4)/2, half (j%4)&1
+    const int vj = lane & 15;
+    const int vkey = 4 * kg + (vj >> 2);
+    const int vsw = vkey & 7;
+    uint32_t voff[4];  // for db & 3; chunk bit 3 (db >> 2) is not swizzled: +128 bytes
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            bf16x8 ka[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                ka[kb] = as_bf16x8(ld16(&sm.k[(kb * 16 + lq) * Smem::KS + 32 * kc + 8 * kg]));
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma16x16x32(ka[kb], qf[kc], sc[kb]);
-        }
-
-        // scale and mask; key of sc[kb][e] within the tile is kb*16 + 4*kg + e
-        if (i < ncache) {
-            const int lim = c1 - (c0 + ((i + trot) % ncache) * kBlockN);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = kb * 16 + 4 * kg + e;
-                    sc[kb][e] = (j < lim) ? sc[kb][e] * a.scale_log2 : -INFINITY;
-                }
-        } else {
-            const int pt = i - ncache;
-            const int wi = 2 * pt;
-            const uint32_t w0 = mwords[lt * a.nw + wi];
-            const uint32_t w1 = (wi + 1 < a.nw) ? mwords[lt * a.nw + wi + 1] : 0u;
-            const int lim = tok_hi - pt * kBlockN;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = kb * 16 + 4 * kg + e;
-                    const uint32_t wd = (j < 32) ? w0 : w1;
-                    const bool vis = (j < lim) && ((wd >> (j & 31)) & 1u);
-                    sc[kb][e] = vis ? sc[kb][e] * a.scale_log2 : -INFINITY;
-                }
-        }
-
-        // online softmax (per query column; the four k-groups hold disjoint keys)
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[kb][e]);
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float mnew = fmaxf(mrun, tmax);
-        const float alpha = fast_exp2(mrun - mnew);
-        mrun = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sc[kb][e] = fast_exp2(sc[kb][e] - mnew);
-                psum += sc[kb][e];
-            }
-        lpart = lpart * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-
-        // O^T += V^T P^T, two k-steps of 32 keys: slots 0-3 hold keys
-        // 32*ks + 4*kg + (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pb[e] = static_cast<__bf16>(sc[2 * ks][e]);
-                pb[4 + e] = static_cast<__bf16>(sc[2 * ks + 1][e]);
-            }
-            uint4 vv[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const uint16_t *vrow = &sm.vt[(db * 16 + lq) * Smem::VS + 32 * ks + 4 * kg];
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16);
-                vv[db] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = mfma16x16x32(as_bf16x8(vv[db]), pb, o[db]);
-        }
-    };
-
-    // Two-stage ring: tile j's K/V loads are issued two tiles ahead into
-    // register slot j % 2 and written to LDS buffer j % 2 just before use;
-    // loads complete in issue order, so each wait covers only the oldest
-    // stage.  One barrier per tile: buffer j % 2 is rewritten only after
-    // every wave has passed the barrier of tile j + 1.
-    uint4 kreg[2][KLD];
-    uint4 vreg[2][4];
-    const int ntile_pad = (ntile + 1) & ~1;
-    load_tile(kreg[0], vreg[0], 0);
-    load_tile(kreg[1], vreg[1], 1);
-    for (int i0 = 0; i0 < ntile_pad; i0 += 2) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int i = i0 + st;
-            store_tile(kreg[st], vreg[st], smem[st]);
-            __syncthreads();
-            if (i < ntile) compute_tile(i, smem[st]);
-            load_tile(kreg[st], vreg[st], i + 2);
-        }
+    for (int d4 = 0; d4 < 4; ++d4) {
+        const int chunk = 2 * d4 + ((vj & 3) >> 1);
+        voff[d4] = TILEB + vkey * ROWB + ((chunk ^ vsw) << 4) + ((vj & 1) << 3);
     }
 
-    float lsum = lpart + shfl_xor(lpart, 16);
-    lsum += shfl_xor(lsum, 32);
-
-    if (a.nsplit == 1) {
-        // o[db][e] = O[query r][d = db*16 + 4*kg + e]
-        if (r < Mpad) {
-            const float inv = (rvalid && lsum > 0.f) ? 1.f / lsum : 0.f;
-            const int pz = r / a.G, hz = g * a.G + r % a.G;
-            uint16_t *orow = a.out + ((static_cast<size_t>(b) * a.P + pz) * a.Hq + hz) * D;
+    f32x4 o[QPW][NDB];
+    float mrun[QPW], lpart[QPW];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                u16x4 w = {f32_to_bf16_bits(o[db][0] * inv), f32_to_bf16_bits(o[db][1] * inv),
-                           f32_to_bf16_bits(o[db][2] * inv), f32_to_bf16_bits(o[db][3] * inv)};
-                *reinterpret_cast<u16x4 *>(orow + db * 16 + 4 * kg) = w;
+    for (int qi = 0; qi < QPW; ++qi) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[qi][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mrun[qi] = kNegBig;
+        lpart[qi] = 0.f;
+    }
+
+    // One pass over the tile for query blocks q0 .. q0+QG-1.
+    constexpr int QG = QPW < 2 ? QPW : 2;
+    auto compute_group = [&](int i, uint32_t sbase, int q0) {
+        const uint8_t *st = stage + (sbase - lds0);
+        // S^T for 64 keys x 16 queries per block; the K fragments of a
+        // head-dim step are read once (one step ahead) for all blocks of the
+        // pass.  Scores stay unscaled: the scale folds into the exponent.
+        f32x4 sc[QG][4];
+#pragma unroll
+        for (int qi = 0; qi < QG; ++qi)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sc[qi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ka[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) ka[0][kb] = *reinterpret_cast<const bf16x8 *>(st + koff[0] + kb * 16 * ROWB);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            if (kc + 1 < NKC)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    ka[(kc + 1) & 1][kb] = *reinterpret_cast<const bf16x8 *>(st + koff[kc + 1] + kb * 16 * ROWB);
+#pragma unroll
+            for (int qi = 0; qi < QG; ++qi)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[q0 + qi][kc], sc[qi][kb]);
+        }
+
+        // mask (partial cache tiles and packed tiles only), online softmax;
+        // key of sc[qi][kb][e] within the tile is kb*16 + 4*kg + e
+        const bool cache = i < ncache;
+        const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
+        const int lim = cache ? c1 - (c0 + ic * kBlockN) : tok_hi - (i - ncache) * kBlockN;
+        const bool full = cache && lim >= kBlockN;  // wave-uniform
+        const int wi = 2 * (i - ncache);
+        if (!full) {
+#pragma unroll
+            for (int qi = 0; qi < QG; ++qi) {
+                uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
+                if (!cache) {
+                    w0 = mwords[lt[q0 + qi] * a.nw + wi];
+                    w1 = (wi + 1 < a.nw) ? mwords[lt[q0 + qi] * a.nw + wi + 1] : 0u;
+                }
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = kb * 16 + 4 * kg + e;
+                        const uint32_t wd = (j < 32) ? w0 : w1;
+                        const bool vis = (j < lim) && ((wd >> (j & 31)) & 1u);
+                        sc[qi][kb][e] = vis ? sc[qi][kb][e] : -INFINITY;
+                    }
             }
         }
-    } else if (rvalid) {
-        const size_t prow = ((static_cast<size_t>(b) * a.Hkv + g) * a.nsplit + s) * (a.nqblk * kBlockM) + r;
-        float *orow = a.ws_o + prow * D;
+        bf16x8 pb[QG][2];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4 *>(orow + db * 16 + 4 * kg) = o[db];
-        if (kg == 0) a.ws_ml[prow] = make_float2(mrun, lsum);
+        for (int qi = 0; qi < QG; ++qi) {
+            const int q = q0 + qi;
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[qi][kb][e]);
+            tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+            tmax *= a.scale_log2;  // the scale is positive
+            // Lazy rescale: the reference max moves only when some row's max
+            // has grown by more than kRescale (log2 units), so O and l stay
+            // in registers untouched on most tiles.  Exact: O and l are both
+            // taken relative to the same reference, and probabilities stay
+            // below 2^kRescale.
+            if (__any(tmax > mrun[q] + kRescale)) {
+                const float mnew = fmaxf(mrun[q], tmax);
+                const float alpha = fast_exp2(mrun[q] - mnew);
+                mrun[q] = mnew;
+                lpart[q] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[q][db] *= alpha;
+            }
+            const float mref = mrun[q];
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sc[qi][kb][e] = fast_exp2(fmaf(sc[qi][kb][e], a.scale_log2, -mref));
+                    psum += sc[qi][kb][e];
+                }
+            lpart[q] += psum;
+            // P^T as the B operand of the two 32-key steps: slots 0-3 hold
+            // keys 32*ks + 4*kg + (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pb[qi][ks][e] = static_cast<__bf16>(sc[qi][2 * ks][e]);
+                    pb[qi][ks][4 + e] = static_cast<__bf16>(sc[qi][2 * ks + 1][e]);
+                }
+        }
+
+        // O^T += V^T P^T over 2*NDB steps (ks, db); each V^T fragment (two
+        // transpose loads) serves every block of the pass and is read kVPre
+        // steps ahead
+        constexpr int NSTEP = 2 * NDB;
+        constexpr int kVPre = 4;
+        auto vaddr = [&](int n) {
+            const int ks = n / NDB, db = n % NDB;
+            return sbase + voff[db & 3] + (db >> 2) * 128 + ks * 32 * ROWB;
+        };
+        bf16x4 vlo[kVPre], vhi[kVPre];
+#pragma unroll
+        for (int n = 0; n < kVPre; ++n) {
+            vlo[n] = lds_read_tr16(vaddr(n));
+            vhi[n] = lds_read_tr16(vaddr(n) + 16 * ROWB);
+        }
+#pragma unroll
+        for (int n = 0; n < NSTEP; ++n) {
+            bf16x8 vf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vf[e] = vlo[n % kVPre][e];
+                vf[4 + e] = vhi[n % kVPre][e];
+            }
+            if (n + kVPre < NSTEP) {
+                vlo[n % kVPre] = lds_read_tr16(vaddr(n + kVPre));
+                vhi[n % kVPre] = lds_read_tr16(vaddr(n + kVPre) + 16 * ROWB);
+            }
+            const int ks = n / NDB, db = n % NDB;
+#pragma unroll
+            for (int qi = 0; qi < QG; ++qi) o[q0 + qi][db] = mfma16x16x32(vf, pb[qi][ks], o[q0 + qi][db]);
+        }
+    };
+    auto compute_tile = [&](int i, uint32_t sbase) {
+#pragma unroll
+        for (int q0 = 0; q0 < QPW; q0 += QG) compute_group(i, sbase, q0);
+    };
+
+    // Ring of kStages LDS stages.  Tiles 0..kStages-2 are issued up front.
+    // At the top of tile i this wavefront's loads of tile i have landed once
+    // at most (kStages-2)*2*NLD of its loads remain outstanding; the barrier
+    // publishes every wavefront's share and certifies that all reads of the
+    // slot of tile i-1 are done, so tile i+kStages-1 may be loaded into it.
+    // Tiles past the last still issue their loads, all out of range, so
+    // every wait counts the same number of loads.
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st) issue_tile(st, st);
+    int cslot = 0, lslot_ring = kStages - 1;  // slots of the tile computed / loaded
+    for (int i = 0; i < ntile; ++i) {
+        vm_wait<(kStages - 2) * 2 * NLD>();
+        __syncthreads();
+        issue_tile(i + kStages - 1, lslot_ring);
+        if (wave_active) compute_tile(i, lds0 + cslot * STAGEB);
+        cslot = (cslot + 1 == kStages) ? 0 : cslot + 1;
+        lslot_ring = (lslot_ring + 1 == kStages) ? 0 : lslot_ring + 1;
+    }
+    vm_wait<0>();
+
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+        float lsum = lpart[qi] + shfl_xor(lpart[qi], 16);
+        lsum += shfl_xor(lsum, 32);
+        const int r = row0 + (NWAVE * qi + wave) * 16 + lq;
+        const bool rvalid = r < Mb;
+        if (a.nsplit == 1) {
+            // o[qi][db][e] = O[query r][d = db*16 + 4*kg + e]; padding rows get zeros
+            if (r < Mpad) {
+                const float inv = (rvalid && lsum > 0.f) ? 1.f / lsum : 0.f;
+                const int pz = r / a.G, hz = g * a.G + r % a.G;
+                uint16_t *orow = a.out + ((static_cast<size_t>(b) * a.P + pz) * a.Hq + hz) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    u16x4 w = {f32_to_bf16_bits(o[qi][db][0] * inv), f32_to_bf16_bits(o[qi][db][1] * inv),
+                               f32_to_bf16_bits(o[qi][db][2] * inv), f32_to_bf16_bits(o[qi][db][3] * inv)};
+                    *reinterpret_cast<u16x4 *>(orow + db * 16 + 4 * kg) = w;
+                }
+            }
+        } else if (rvalid) {
+            const size_t prow = ((static_cast<size_t>(b) * a.Hkv + g) * a.nsplit + s) * a.rows_unit + r;
+            float *orow = a.ws_o + prow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4 *>(orow + db * 16 + 4 * kg) = o[qi][db];
+            if (kg == 0) a.ws_ml[prow] = make_float2(mrun[qi], lsum);
+        }
     }
 }
 
@@ -350,19 +431,20 @@ __global__ __launch_bounds__(256) void k_tree_attn_bf16(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
     constexpr int KCH4 = D / 4;  // float4 chunks per row
-    __shared__ float wgt[kBlockM][kMaxSplits + 1];
-    const int qb = blockIdx.x % a.nqblk;
-    const int bg = blockIdx.x / a.nqblk;
+    __shared__ float wgt[kCombRows][kMaxSplits + 1];
+    const int nrb = a.rows_unit / kCombRows;
+    const int qb = blockIdx.x % nrb;
+    const int bg = blockIdx.x / nrb;
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
     const int Pb = min(max(a.plen[b], 0), a.P);
     const int Mb = a.G * Pb;
     const int Mpad = a.G * a.P;
-    const int row0 = qb * kBlockM;
-    const size_t split_stride = static_cast<size_t>(a.nqblk) * kBlockM;
+    const int row0 = qb * kCombRows;
+    const size_t split_stride = static_cast<size_t>(a.rows_unit);
     const size_t base = (static_cast<size_t>(b) * a.Hkv + g) * a.nsplit * split_stride;
 
-    if (threadIdx.x < kBlockM) {
+    if (threadIdx.x < kCombRows) {
         const int r = row0 + threadIdx.x;
         if (r < Mb) {
             float M = kNegBig;
@@ -379,7 +461,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kBlockM * KCH4; i += 256) {
+    for (int i = threadIdx.x; i < kCombRows * KCH4; i += 256) {
         const int rl = i / KCH4;
         const int c = i % KCH4;
         const int r = row0 + rl;
@@ -485,27 +567,34 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max) {
-    AttnPlan plan{0, 1, kBlockN, 0};
+    AttnPlan plan{0, 1, kBlockN, 0, 1, 0, 4};
     if (dtype != 1) return plan;  // fp32 path needs no workspace
     const int G = Hq / Hkv;
-    plan.nqblk = (G * P_max + kBlockM - 1) / kBlockM;
-    // Split the cache only as far as needed for about four workgroups per
-    // CU, and never below 16 key tiles (1024 keys) per split: shorter
-    // splits spend more on partial writes and the merge than they gain in
-    // parallelism (measured on MI355X).
+    const int rows = G * P_max;
+    // 16-row query blocks per wavefront: enough that one workgroup holds all
+    // rows of a (request, KV head) whenever they fit in 256
+    // (QPW, wavefronts) = (1, 4), (2, 4) or (2, 8): 64, 128 or 256 rows
+    plan.qpw = rows <= 64 ? 1 : 2;
+    plan.nwave = rows <= 128 ? 4 : 8;
+    const int rb = 16 * plan.qpw * plan.nwave;
+    plan.nqblk = (rows + rb - 1) / rb;
+    plan.rows_unit = plan.nqblk * rb;
+    // One workgroup per CU fits (the LDS ring): split the cache only as far
+    // as needed to give every CU a workgroup, and never below 8 key tiles
+    // per split.
     const long units = static_cast<long>(B) * Hkv * plan.nqblk;
     const int tiles = (S_max + kBlockN - 1) / kBlockN;
-    const long target = 4L * device_cu_count();
+    const long target = device_cu_count();
     int nsplit = static_cast<int>((target + units - 1) / units);
-    nsplit = min(nsplit, max(1, tiles / 16));
+    nsplit = min(nsplit, max(1, tiles / 8));
     nsplit = env_int("RD_ATTN_SPLITS", nsplit);
     nsplit = max(1, min(nsplit, min(max(tiles, 1), kMaxSplits)));
     const int chunk_tiles = (max(tiles, 1) + nsplit - 1) / nsplit;
     plan.nsplit = (max(tiles, 1) + chunk_tiles - 1) / chunk_tiles;
     plan.chunk = chunk_tiles * kBlockN;
     if (plan.nsplit > 1) {
-        const size_t rows = static_cast<size_t>(B) * Hkv * plan.nsplit * plan.nqblk * kBlockM;
-        plan.ws_bytes = rows * (static_cast<size_t>(D) * sizeof(float) + sizeof(float2));
+        const size_t nrow = static_cast<size_t>(B) * Hkv * plan.nsplit * plan.rows_unit;
+        plan.ws_bytes = nrow * (static_cast<size_t>(D) * sizeof(float) + sizeof(float2));
     }
     return plan;
 }
@@ -546,18 +635,25 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
     a.nqblk = plan.nqblk;
     a.nsplit = plan.nsplit;
     a.chunk = plan.chunk;
+    a.rows_unit = plan.rows_unit;
     a.out = static_cast<uint16_t *>(out);
-    const size_t rows = static_cast<size_t>(B) * Hkv * plan.nsplit * plan.nqblk * kBlockM;
+    const size_t nrow = static_cast<size_t>(B) * Hkv * plan.nsplit * plan.rows_unit;
     a.ws_o = static_cast<float *>(ws);
-    a.ws_ml = (plan.nsplit > 1) ? reinterpret_cast<float2 *>(static_cast<float *>(ws) + rows * D) : nullptr;
-    const unsigned nblk = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * plan.nsplit * plan.nqblk);
-    if (D == 64)
-        hipLaunchKernelGGL(k_tree_attn_bf16<64>, dim3(nblk), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(k_tree_attn_bf16<128>, dim3(nblk), dim3(256), 0, stream, a);
+    a.ws_ml = (plan.nsplit > 1) ? reinterpret_cast<float2 *>(static_cast<float *>(ws) + nrow * D) : nullptr;
+    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * Hkv * plan.nsplit * plan.nqblk));
+    const dim3 blk(64 * plan.nwave);
+    if (D == 64) {
+        if (plan.qpw == 1) hipLaunchKernelGGL((k_tree_attn_bf16<64, 1, 4>), grid, blk, 0, stream, a);
+        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 8>), grid, blk, 0, stream, a);
+    } else {
+        if (plan.qpw == 1) hipLaunchKernelGGL((k_tree_attn_bf16<128, 1, 4>), grid, blk, 0, stream, a);
+        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 8>), grid, blk, 0, stream, a);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || plan.nsplit == 1) return err;
-    const unsigned ncomb = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * plan.nqblk);
+    const unsigned ncomb = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * (plan.rows_unit / kCombRows));
     if (D == 64)
         hipLaunchKernelGGL(k_attn_combine<64>, dim3(ncomb), dim3(256), 0, stream, a);
     else

@@ -22,6 +22,9 @@ struct AttnPlan {
     int nsplit;     // KV-cache splits
     int chunk;      // cache keys per split (multiple of the key tile)
     size_t ws_bytes;
+    int qpw;        // 16-row query blocks per wavefront (1 or 2)
+    int rows_unit;  // nqblk * rows per workgroup
+    int nwave;      // wavefronts per workgroup (4 or 8)
 };
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max);
 hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *k_new,
