@@ -147,16 +147,16 @@ int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_
     if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
     if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
     hipStream_t s = as_stream(stream);
+    int64_t row_bytes = 0;
     if (packed && unpacked && row_len > 0) {
-        const int64_t row_bytes = row_len * (dtype == RD_F32 ? 4 : 2);
+        row_bytes = row_len * (dtype == RD_F32 ? 4 : 2);
         const int64_t rows = static_cast<int64_t>(B) * W * L;
         const int64_t chunks = (row_bytes + 1023) / 1024;  // upper bound on blocks per row
         if (rows * chunks * 256 >= (1LL << 32)) return RD_E_UNSUPPORTED;
-        const hipError_t e = rd::launch_unpack(packed, unpacked, unpacker, row_bytes, B, W, L, s);
-        if (e != hipSuccess) return RD_E_HIP;
     }
-    return hip_status(rd::launch_accept(beams, unpacker, packed_argmax, B, W, L, match_len, best_beam, accept_len,
-                                        accepted_tokens, s));
+    return hip_status(rd::launch_unpack_accept(row_bytes ? packed : nullptr, row_bytes ? unpacked : nullptr, unpacker,
+                                               row_bytes, beams, packed_argmax, B, W, L, match_len, best_beam,
+                                               accept_len, accepted_tokens, s));
 }
 
 }  // extern "C"

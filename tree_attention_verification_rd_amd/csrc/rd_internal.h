@@ -48,11 +48,10 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
                           int32_t *argmax, void *ws, hipStream_t stream);
 
 // unpack gather + accept
-hipError_t launch_unpack(const void *packed, void *unpacked, const int32_t *unpacker,
-                         int64_t row_bytes, int B, int W, int L, hipStream_t stream);
-hipError_t launch_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *pargmax,
-                         int B, int W, int L, int32_t *match_len, int32_t *best_beam,
-                         int32_t *accept_len, int32_t *accepted, hipStream_t stream);
+hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,
+                                const int32_t *beams, const int32_t *pargmax, int B, int W, int L,
+                                int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
+                                int32_t *accepted, hipStream_t stream);
 
 int device_cu_count();
 

@@ -6,7 +6,8 @@
 // accumulators with the lowest vocabulary id winning ties.
 //
 // bf16 GEMM layout.  Only valid packed rows (p < packed_len[b]) are
-// computed: a small kernel compacts them into a row map.  The product is
+// computed: every workgroup numbers them itself with a prefix sum over the
+// packed lengths (no separate pass, no launch).  The product is
 // formed transposed, C^T = W X^T (A operand = weight rows, B operand =
 // hidden rows), so each lane's accumulator holds four consecutive
 // vocabulary entries of one row -- what the argmax epilogue and the logits
@@ -20,6 +21,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "rd_common.h"
 #include "rd_internal.h"
 
@@ -27,12 +30,10 @@ namespace rd {
 
 namespace {
 
-constexpr int kBK = 64;
 
 struct LmArgs {
     const uint16_t *hidden, *weight;
-    const int32_t *rowmap;
-    const int32_t *rcount;
+    const int32_t *plen;  // packed lengths [B] (clamped to [0, P]); null: all P rows valid
     int B, P, K, V;
     uint16_t *logits;
     float *pval;
@@ -50,55 +51,82 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// valid rows -> compact row map (rowmap[m] = b*P + p), and their count
-__global__ __launch_bounds__(256) void k_rowmap(const int32_t *__restrict__ plen, int B, int P,
-                                                int32_t *__restrict__ rowmap, int32_t *__restrict__ rcount) {
-    __shared__ int scan[256];
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int b0 = 0; b0 < B; b0 += 256) {
-        const int b = b0 + threadIdx.x;
-        const int n = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
-        scan[threadIdx.x] = n;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int add = (threadIdx.x >= off) ? scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            scan[threadIdx.x] += add;
-            __syncthreads();
-        }
-        const int start = carry + scan[threadIdx.x] - n;
-        for (int p = 0; p < n; ++p) rowmap[start + p] = b * P + p;
-        __syncthreads();
-        if (threadIdx.x == 255) carry += scan[255];
-        __syncthreads();
+// Block-wide inclusive prefix sum of one value per thread (256 threads);
+// `tot` receives the sum.  `scratch` holds 4 ints.
+__device__ __forceinline__ int block_scan256(int v, int *scratch, int &tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
     }
-    if (threadIdx.x == 0) *rcount = carry;
+    if (lane == 63) scratch[wave] = v;
+    __syncthreads();
+    int before = 0;
+    tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int sw = scratch[w];
+        before += (w < wave) ? sw : 0;
+        tot += sw;
+    }
+    __syncthreads();
+    return v + before;
 }
 
-template <int WV, int WR, int GV, int GR, int NS>
+// Valid rows (p < packed_len[b]) are numbered in (b, p) order -- the compact
+// rows.  Pass 1 counts them; pass 2 records, for compact rows r0 .. r0+n-1,
+// the packed row b*P + p each one stands for.
+__device__ int count_rows(const int32_t *plen, int B, int P, int *scratch) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 256) {
+        const int b = b0 + static_cast<int>(threadIdx.x);
+        const int n = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
+        int tot;
+        block_scan256(n, scratch, tot);
+        carry += tot;
+    }
+    return carry;
+}
+__device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32_t *rmap, int *scratch) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 256) {
+        const int b = b0 + static_cast<int>(threadIdx.x);
+        const int cnt = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
+        int tot;
+        const int start = carry + block_scan256(cnt, scratch, tot) - cnt;
+        const int lo = max(start, r0), hi = min(start + cnt, r0 + n);
+        for (int m = lo; m < hi; ++m) rmap[m - r0] = b * P + (m - start);
+        carry += tot;
+    }
+}
+
+template <int WV, int WR, int GV, int GR, int NS, int BK>
 __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     static_assert(GV * GR == 4, "four wavefronts per workgroup");
     static_assert(NS >= 2, "the ring needs a stage in flight while another is consumed");
-    static_assert(kBK == 64, "two 32-wide halves per k-step");
+    static_assert(BK == 32 || BK == 64, "one or two 32-wide MFMA steps per k-step");
+    constexpr int NSUB = BK / 32;            // MFMA k-steps per staged k-step
     constexpr int BV = GV * WV;              // vocabulary rows per tile
     constexpr int BR = GR * WR;              // compact hidden rows per tile
     constexpr int NVB = WV / 16;
     constexpr int NRB = WR / 16;
-    constexpr int kRowB = kBK * 2;           // bytes of one staged row (one cache line)
+    constexpr int kRowB = BK * 2;            // bytes of one staged row (a cache line or half of one)
+    constexpr int CPR = BK / 8;              // 16-byte chunks per staged row
+    constexpr int RPL = 1024 / kRowB;        // rows per 1 KB load instruction
     constexpr int kStageRows = BV + BR;
     constexpr int kStageBytes = kStageRows * kRowB;
-    static_assert(kStageRows % 32 == 0, "whole 8-row loads, shared evenly by the wavefronts");
-    constexpr int NL = kStageRows / 32;      // LDS loads per wavefront per stage
-    constexpr int NLW = BV / 32;             // ... of weight rows
-    constexpr int NLX = BR / 32;             // ... of hidden rows
-    static_assert(BV % 32 == 0 && BR % 32 == 0, "each wavefront loads whole groups of both operands");
+    constexpr int NL = kStageRows / RPL / 4; // LDS loads per wavefront per stage
+    constexpr int NLW = BV / RPL / 4;        // ... of weight rows
+    constexpr int NLX = BR / RPL / 4;        // ... of hidden rows
+    static_assert(BV % (4 * RPL) == 0 && BR % (4 * RPL) == 0, "each wavefront loads whole groups of both operands");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * kStageBytes];
+    __shared__ int32_t rmap[BR];  // packed row (b*P + p) of each compact row of the tile
+    __shared__ int scan_tmp[4];
 
     // wave-uniform values are read into scalar registers explicitly so the
     // buffer resources built from them stay scalar (no per-lane loops)
-    const int R = __builtin_amdgcn_readfirstlane(*a.rcount);
+    const int R = __builtin_amdgcn_readfirstlane(count_rows(a.plen, a.B, a.P, scan_tmp));
     const int nrt = (R + BR - 1) / BR;       // row tiles that hold valid rows
     const int ntiles = nrt * a.nvt;
     const int tid = threadIdx.x;
@@ -109,26 +137,27 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     const int gv = wave % GV;
     const int gr = wave / GV;
     const int K = a.K;
-    const int nk = (K + kBK - 1) / kBK;
+    const int nk = (K + BK - 1) / BK;
     const uint32_t rowb = static_cast<uint32_t>(K) * 2;
 
-    // Staging.  A stage holds BV weight rows then BR hidden rows, kBK
-    // columns each, one 128-byte line per row.  Each load instruction moves
-    // 8 whole rows (coalesced cache lines); within a row the eight 16-byte
-    // chunks are stored XOR-swizzled by (row % 8), so the fragment reads
-    // below (16 rows x one chunk per instruction) hit distinct banks.  Lane
-    // i of a load covers staged row 8j + i/8 and stores LDS slot i%8, which
-    // holds chunk c = (i%8) ^ (i/8) of that row.  Load j = 4*i + wave is
-    // the wavefront's i-th: its first BV/32 loads are weight rows, the rest
+    // Staging.  A stage holds BV weight rows then BR hidden rows, BK
+    // columns each (128 or 64 bytes per row).  Each load instruction moves
+    // RPL whole rows; within a row the 16-byte chunks are stored XOR-swizzled
+    // (by row & 7 for 8 chunks, by (row >> 1) & 3 for 4), so the fragment
+    // reads below (16 rows x one chunk per instruction) hit distinct banks.
+    // Lane i of a load covers staged row RPL*j + i/CPR and stores LDS slot
+    // i % CPR, which holds chunk slot ^ swizzle(row).  Load j = 4*i + wave
+    // is the wavefront's i-th: its first NLW loads are weight rows, the rest
     // hidden rows.
-    const int lrow = lane >> 3;
-    const int lchunk = (lane & 7) ^ lrow;
+    auto swz = [](int row) { return CPR == 8 ? (row & 7) : ((row >> 1) & 3); };
+    const int lrow = lane / CPR;
+    const int lchunk = (lane % CPR) ^ swz(lrow);
     const i32x4_t xres = make_srsrc(a.hidden, static_cast<uint32_t>(static_cast<size_t>(a.B) * a.P * K * 2));
     const uint32_t lds0 = lds_addr_of(lds);
     // fragment reads: lane reads row lq of each 16-row block, k-chunk
     // 4*ks + kg, at its swizzled slot; the ks = 1 slot is the ks = 0 slot
     // with chunk bit 2 flipped
-    const uint32_t sw = static_cast<uint32_t>((kg ^ (lq & 7)) << 4);
+    const uint32_t sw = static_cast<uint32_t>((kg ^ swz(lq)) << 4);
     const uint32_t aoff = static_cast<uint32_t>(gv * WV + lq) * kRowB + sw;
     const uint32_t boff = static_cast<uint32_t>(BV + gr * WR + lq) * kRowB + sw;
     // All workgroups on one XCD (block i runs on XCD i % 8) walk K in the
@@ -156,29 +185,31 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         const int vt = within / gsz;
         const int r0 = rt * BR;
         const int v0 = vt * BV;
+        map_rows(a.plen, a.B, a.P, r0, min(BR, R - r0), rmap, scan_tmp);
+        __syncthreads();
 
         const int wrows = max(0, min(a.V - v0, BV));
         const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(v0, a.V)) * K,
                                         static_cast<uint32_t>(wrows) * rowb);
         // weight rows past V fall outside wres; hidden rows past R get kOOB
-        const uint32_t wbase = static_cast<uint32_t>(8 * wave + lrow) * rowb + 16 * lchunk;
+        const uint32_t wbase = static_cast<uint32_t>(RPL * wave + lrow) * rowb + 16 * lchunk;
         uint32_t xbase[NLX];
 #pragma unroll
         for (int i = 0; i < NLX; ++i) {
-            const int m = r0 + 8 * (4 * (NLW + i) + wave) + lrow - BV;
-            xbase[i] = (m < R) ? static_cast<uint32_t>(a.rowmap[m]) * rowb + 16 * lchunk : kOOB;
+            const int m = r0 + RPL * (4 * (NLW + i) + wave) + lrow - BV;
+            xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
         }
         // Stage kt (k-step (kt + krot) mod nk) goes to ring slot kt % NS.
         // Stages past the last k-step still issue their loads, all out of
         // range (zeros), so every wait below counts the same number of loads.
         auto issue_stage = [&](int kt, int slot) {
             const int kr = (kt < nk) ? ((kt + krot >= nk) ? kt + krot - nk : kt + krot) : -1;
-            const bool kin = kr >= 0 && kr * kBK + 8 * lchunk < K;
+            const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
             const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
             const uint32_t sbase = lds0 + slot * kStageBytes + wave * 1024;
 #pragma unroll
             for (int i = 0; i < NLW; ++i)
-                lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 32 * rowb + kadd : kOOB);
+                lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 4 * RPL * rowb + kadd : kOOB);
 #pragma unroll
             for (int i = 0; i < NLX; ++i)
                 lds_dma16(sbase + (NLW + i) * 4096, xres, kin ? xbase[i] + kadd : kOOB);
@@ -199,12 +230,13 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         // reads of slot (kt-1) % NS are done, so stage kt+NS-1 may be loaded
         // into it.
         //
-        // Fragments are software-pipelined across the barrier: the second
-        // half (k 32..63) of k-step kt is read into registers before the
-        // barrier of k-step kt+1 and multiplied after it, while the
-        // first-half reads of k-step kt+1 are in flight, so LDS latency does
-        // not stall the MFMAs.  (The first k-step multiplies zero fragments
-        // in that slot.)
+        // Fragments are software-pipelined across the barrier: the last
+        // 32-wide MFMA step of k-step kt is read into registers before the
+        // barrier of k-step kt+1 and multiplied after it, while the first
+        // reads of k-step kt+1 are in flight, so LDS latency does not stall
+        // the MFMAs.  (The first k-step multiplies zero fragments in that
+        // slot.)  With one MFMA step per k-step the two fragment buffers
+        // alternate between k-steps.
         auto read_frags = [&](const uint8_t *st, uint32_t x, bf16x8 (&fa)[NVB], bf16x8 (&fb)[NRB]) {
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb)
@@ -219,39 +251,52 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = mfma16x16x32(fa[vb], fb[rb], acc[vb][rb]);
         };
-        bf16x8 ha[NVB], hb[NRB];  // second half of the previous k-step
+        bf16x8 fa2[2][NVB], fb2[2][NRB];  // [1]: the held (previous) step
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) ha[vb] = bf16x8{};
+        for (int vb = 0; vb < NVB; ++vb) fa2[1][vb] = bf16x8{};
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) hb[rb] = bf16x8{};
+        for (int rb = 0; rb < NRB; ++rb) fb2[1][rb] = bf16x8{};
 
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s) issue_stage(s, s);
 
-        for (int kt0 = 0; kt0 < nk; kt0 += NS) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int kt = kt0 + s;
-                if (kt >= nk) break;
-                vm_wait<(NS - 2) * NL>();
-                __syncthreads();
-                issue_stage(kt + NS - 1, (s + NS - 1) % NS);
-                if (active) {
-                    const uint8_t *st = lds + s * kStageBytes;
-                    bf16x8 fa[NVB], fb[NRB];
-                    read_frags(st, 0u, fa, fb);
-                    mma(ha, hb);
-                    read_frags(st, 64u, ha, hb);
-                    mma(fa, fb);
+        // The k loop is unrolled by two (the fragment buffers alternate);
+        // ring slots are tracked at run time.
+        int cslot = 0;  // slot of k-step kt
+        auto step = [&](int kt, auto cur_c) {
+            constexpr int cur = decltype(cur_c)::value;  // fragment buffer of this k-step
+            vm_wait<(NS - 2) * NL>();
+            __syncthreads();
+            const int lslot = (cslot == 0) ? NS - 1 : cslot - 1;  // (kt + NS - 1) % NS
+            issue_stage(kt + NS - 1, lslot);
+            if (active) {
+                const uint8_t *st = lds + cslot * kStageBytes;
+                if constexpr (NSUB == 2) {
+                    read_frags(st, 0u, fa2[0], fb2[0]);
+                    mma(fa2[1], fb2[1]);
+                    read_frags(st, 64u, fa2[1], fb2[1]);
+                    mma(fa2[0], fb2[0]);
                     // keep that order: reads, multiplies, reads, multiplies
                     __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
+                } else {
+                    read_frags(st, 0u, fa2[cur], fb2[cur]);
+                    mma(fa2[cur ^ 1], fb2[cur ^ 1]);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
                 }
             }
+            cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
+        };
+        // An odd k-step count gets one padding step (its loads are out of
+        // range, so it multiplies zeros); the held buffer is then always [1].
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
         }
-        if (active) mma(ha, hb);
+        if (active) mma(fa2[1], fb2[1]);
         vm_wait<0>();
         __syncthreads();  // the padding stages' loads have landed before LDS is reused
 
@@ -267,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
             if (active) {
-                const int pr = mvalid ? a.rowmap[m] : 0;
+                const int pr = mvalid ? rmap[m - r0] : 0;
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) {
                     const int v = v0 + gv * WV + vb * 16 + 4 * kg;
@@ -305,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             if (kg == 0) {
                 if (GV == 1) {
                     if (mvalid) {
-                        const size_t pr = static_cast<size_t>(a.rowmap[m]);
+                        const size_t pr = static_cast<size_t>(rmap[m - r0]);
                         a.pval[pr * a.nvt + vt] = bv;
                         a.pidx[pr * a.nvt + vt] = bi;
                     }
@@ -327,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
                         bv = redv[g * BR + i];
                         bi = redi[g * BR + i];
                     }
-                const size_t pr = static_cast<size_t>(a.rowmap[r0 + i]);
+                const size_t pr = static_cast<size_t>(rmap[i]);
                 a.pval[pr * a.nvt + vt] = bv;
                 a.pidx[pr * a.nvt + vt] = bi;
             }
@@ -439,7 +484,7 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
     }
     plan.nvt = (V + plan.vtile - 1) / plan.vtile;
     const size_t rows = static_cast<size_t>(plan.rows_pad);
-    plan.ws_bytes = 256 + align256(rows * 4) + 2 * align256(rows * plan.nvt * 4);
+    plan.ws_bytes = 2 * align256(rows * plan.nvt * 4);
     return plan;
 }
 
@@ -447,23 +492,19 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
                           const void *weight, int B, int P_max, int K, int V, void *logits, int32_t *argmax,
                           void *ws, hipStream_t stream) {
     char *w = static_cast<char *>(ws);
-    int32_t *rcount = reinterpret_cast<int32_t *>(w);
-    int32_t *rowmap = reinterpret_cast<int32_t *>(w + 256);
     const size_t rows = static_cast<size_t>(plan.rows_pad);
-    float *pval = reinterpret_cast<float *>(w + 256 + align256(rows * 4));
-    int32_t *pidx = reinterpret_cast<int32_t *>(w + 256 + align256(rows * 4) + align256(rows * plan.nvt * 4));
+    float *pval = reinterpret_cast<float *>(w);
+    int32_t *pidx = reinterpret_cast<int32_t *>(w + align256(rows * plan.nvt * 4));
 
     if (dtype == 0) {
         hipLaunchKernelGGL(k_lm_head_f32, dim3(static_cast<unsigned>(rows * plan.nvt)), dim3(256), 0, stream,
                            static_cast<const float *>(hidden), plen, static_cast<const float *>(weight), P_max, K,
                            V, static_cast<float *>(logits), pval, pidx, plan.nvt);
     } else {
-        hipLaunchKernelGGL(k_rowmap, dim3(1), dim3(256), 0, stream, plen, B, P_max, rowmap, rcount);
         LmArgs a;
         a.hidden = static_cast<const uint16_t *>(hidden);
         a.weight = static_cast<const uint16_t *>(weight);
-        a.rowmap = rowmap;
-        a.rcount = rcount;
+        a.plen = plen;
         a.B = B;
         a.P = P_max;
         a.K = K;
@@ -475,9 +516,9 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.nrt = static_cast<int>((rows + plan.rtile - 1) / plan.rtile);
         const dim3 grid(static_cast<unsigned>(a.nrt * a.nvt));
         if (plan.variant == 0)
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 64>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 4, 32>), grid, dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -1,19 +1,71 @@
 // Step 3b (unpack gather) and step 4 (greedy accept) kernels.
+#include <type_traits>
+
 #include "rd_common.h"
 #include "rd_internal.h"
 
 namespace rd {
 
+// Greedy accept: one wavefront per request, one lane per beam.  Lane w walks
+// its beam while the draft at j+1 equals the target's choice at j; the best
+// beam is the max of the key (match length, -w) across lanes, so ties go to
+// the lowest beam.
+struct AcceptArgs {
+    const int32_t *beams, *unpacker, *pargmax;
+    int W, L;
+    int32_t *match_len, *best_beam, *accept_len, *accepted;
+};
+
+__device__ __forceinline__ void accept_request(const AcceptArgs &a, int b, int lane) {
+    const int W = a.W, L = a.L;
+    const int P = W * L;
+    const int32_t *am = a.pargmax + static_cast<size_t>(b) * P;
+    auto target_at = [&](int w, int l) {
+        const int slot = a.unpacker[(static_cast<size_t>(b) * W + w) * L + l];
+        return am[min(max(slot, 0), P - 1)];
+    };
+    int n = 0;
+    if (lane < W) {
+        const int32_t *bw = a.beams + (static_cast<size_t>(b) * W + lane) * L;
+        while (n < L - 1 && bw[n + 1] == target_at(lane, n)) ++n;
+        a.match_len[static_cast<size_t>(b) * W + lane] = n;
+    }
+    int key = (lane < W) ? ((n << 6) | (63 - lane)) : -1;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_xor(key, off));
+    const int best = 63 - (key & 63);
+    const int nbest = key >> 6;
+    if (lane == 0) {
+        a.best_beam[b] = best;
+        a.accept_len[b] = nbest;
+    }
+    if (lane < L) {
+        int t = -1;
+        if (lane < nbest)
+            t = a.beams[(static_cast<size_t>(b) * W + best) * L + lane + 1];
+        else if (lane == nbest)
+            t = target_at(best, nbest);
+        a.accepted[static_cast<size_t>(b) * L + lane] = t;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_accept(AcceptArgs a) { accept_request(a, blockIdx.x, threadIdx.x); }
+
 // Unpack, as the PyTorch `unpack` listing of the TensorRT-LLM ReDrafter blog
 // ("Implementing in-Engine Validation and Drafting") defines it:
 // out[b,w,l,:] = packed[b, unpacker[b,w,l], :].  A streaming row copy: each
 // workgroup moves one chunk of one output row with UNROLL independent
-// vector loads in flight per thread.
+// vector loads in flight per thread.  The B workgroups after the copy's run
+// the greedy accept (the two parts are independent), saving a launch.
 template <typename T, int UNROLL>
-__global__ __launch_bounds__(256) void k_unpack_rows(const T *__restrict__ packed, T *__restrict__ out,
-                                                     const int32_t *__restrict__ unpacker,
-                                                     int64_t row_elems, int P, int WL, int nchunks) {
+__global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ packed, T *__restrict__ out,
+                                                       const int32_t *__restrict__ unpacker, int64_t row_elems,
+                                                       int P, int WL, int nchunks, int64_t ncopy, AcceptArgs acc) {
     const int64_t blk = blockIdx.x;
+    if (blk >= ncopy) {
+        if (threadIdx.x < kWave) accept_request(acc, static_cast<int>(blk - ncopy), threadIdx.x);
+        return;
+    }
     const int64_t row = blk / nchunks;
     const int chunk = static_cast<int>(blk % nchunks);
     const int64_t b = row / WL;
@@ -34,83 +86,32 @@ __global__ __launch_bounds__(256) void k_unpack_rows(const T *__restrict__ packe
     }
 }
 
-// Greedy accept: one wavefront per request, one lane per beam.  Lane w walks
-// its beam while the draft at j+1 equals the target's choice at j; the best
-// beam is the max of the key (match length, -w) across lanes, so ties go to
-// the lowest beam.
-__global__ __launch_bounds__(64) void k_accept(const int32_t *__restrict__ beams,
-                                               const int32_t *__restrict__ unpacker,
-                                               const int32_t *__restrict__ pargmax, int W, int L,
-                                               int32_t *__restrict__ match_len,
-                                               int32_t *__restrict__ best_beam,
-                                               int32_t *__restrict__ accept_len,
-                                               int32_t *__restrict__ accepted) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int P = W * L;
-    const int32_t *am = pargmax + static_cast<size_t>(b) * P;
-    auto target_at = [&](int w, int l) {
-        const int slot = unpacker[(static_cast<size_t>(b) * W + w) * L + l];
-        return am[min(max(slot, 0), P - 1)];
-    };
-    int n = 0;
-    if (lane < W) {
-        const int32_t *bw = beams + (static_cast<size_t>(b) * W + lane) * L;
-        while (n < L - 1 && bw[n + 1] == target_at(lane, n)) ++n;
-        match_len[static_cast<size_t>(b) * W + lane] = n;
+hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,
+                                const int32_t *beams, const int32_t *pargmax, int B, int W, int L,
+                                int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
+                                int32_t *accepted, hipStream_t stream) {
+    AcceptArgs acc{beams, unpacker, pargmax, W, L, match_len, best_beam, accept_len, accepted};
+    if (!packed || !unpacked || row_bytes <= 0) {
+        hipLaunchKernelGGL(k_accept, dim3(B), dim3(kWave), 0, stream, acc);
+        return hipGetLastError();
     }
-    int key = (lane < W) ? ((n << 6) | (63 - lane)) : -1;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_xor(key, off));
-    const int best = 63 - (key & 63);
-    const int nbest = key >> 6;
-    if (lane == 0) {
-        best_beam[b] = best;
-        accept_len[b] = nbest;
-    }
-    if (lane < L) {
-        int t = -1;
-        if (lane < nbest)
-            t = beams[(static_cast<size_t>(b) * W + best) * L + lane + 1];
-        else if (lane == nbest)
-            t = target_at(best, nbest);
-        accepted[static_cast<size_t>(b) * L + lane] = t;
-    }
-}
-
-hipError_t launch_unpack(const void *packed, void *unpacked, const int32_t *unpacker,
-                         int64_t row_bytes, int B, int W, int L, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(B) * W * L;
     const int P = W * L;
     const uintptr_t align = reinterpret_cast<uintptr_t>(packed) | reinterpret_cast<uintptr_t>(unpacked);
     constexpr int U = 4;
-    if (row_bytes % 16 == 0 && align % 16 == 0) {
-        const int64_t elems = row_bytes / 16;
+    auto go = [&](auto *src, auto *dst, int64_t elems) {
+        using T = std::remove_const_t<std::remove_pointer_t<decltype(src)>>;
         const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
-        hipLaunchKernelGGL((k_unpack_rows<u32x4, U>), dim3(static_cast<unsigned>(rows * nchunks)),
-                           dim3(256), 0, stream, static_cast<const u32x4 *>(packed),
-                           static_cast<u32x4 *>(unpacked), unpacker, elems, P, W * L, nchunks);
-    } else if (row_bytes % 4 == 0 && align % 4 == 0) {
-        const int64_t elems = row_bytes / 4;
-        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
-        hipLaunchKernelGGL((k_unpack_rows<uint32_t, U>), dim3(static_cast<unsigned>(rows * nchunks)),
-                           dim3(256), 0, stream, static_cast<const uint32_t *>(packed),
-                           static_cast<uint32_t *>(unpacked), unpacker, elems, P, W * L, nchunks);
-    } else {
-        const int64_t elems = row_bytes;
-        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
-        hipLaunchKernelGGL((k_unpack_rows<uint8_t, U>), dim3(static_cast<unsigned>(rows * nchunks)),
-                           dim3(256), 0, stream, static_cast<const uint8_t *>(packed),
-                           static_cast<uint8_t *>(unpacked), unpacker, elems, P, W * L, nchunks);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *pargmax,
-                         int B, int W, int L, int32_t *match_len, int32_t *best_beam,
-                         int32_t *accept_len, int32_t *accepted, hipStream_t stream) {
-    hipLaunchKernelGGL(k_accept, dim3(B), dim3(kWave), 0, stream, beams, unpacker, pargmax, W, L,
-                       match_len, best_beam, accept_len, accepted);
+        const int64_t ncopy = rows * nchunks;
+        hipLaunchKernelGGL((k_unpack_accept<T, U>), dim3(static_cast<unsigned>(ncopy + B)), dim3(256), 0, stream,
+                           src, dst, unpacker, elems, P, W * L, nchunks, ncopy, acc);
+    };
+    if (row_bytes % 16 == 0 && align % 16 == 0)
+        go(static_cast<const u32x4 *>(packed), static_cast<u32x4 *>(unpacked), row_bytes / 16);
+    else if (row_bytes % 4 == 0 && align % 4 == 0)
+        go(static_cast<const uint32_t *>(packed), static_cast<uint32_t *>(unpacked), row_bytes / 4);
+    else
+        go(static_cast<const uint8_t *>(packed), static_cast<uint8_t *>(unpacked), row_bytes);
     return hipGetLastError();
 }
 
