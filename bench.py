@@ -14,6 +14,7 @@ on a bounded sample on this host.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +44,31 @@ def parse():
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run a plain device copy of this size (a known-traffic reference for HBM counters)")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "tree_attention_verification_rd_amd", "csrc")
+CALL_SOURCES = {"lm_head": "rd_lm_head.hip", "attention": "rd_attention.hip"}
+
+
+def counted_traffic(workload: str, call: str):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record for this workload (scaled by a copy of known size), or None when
+    there is no record or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for ln in open(path):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in (CALL_SOURCES[call], "rd_common.h", "rd_internal.h"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    if rec.get(f"{call}.sources_sha256") != h.hexdigest()[:16]:
+        return None
+    return int(rec[f"{call}.traffic_bytes"])
 
 
 def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool):
@@ -197,15 +223,16 @@ def main():
     def roof(call, bound):
         nbytes, flops = work[call]
         t = per_call_us[call] * 1e-6
+        traffic = counted_traffic(cfg.name, call) if full else None
         if bound == "hbm":
             ach = nbytes / t / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "algorithmic_bytes": int(nbytes), "avg_us": round(per_call_us[call], 2)}
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         ach = flops / t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "algorithmic_flops": int(flops),
+                "frac": round(ach / peak, 4), "traffic": traffic, "algorithmic_flops": int(flops),
                 "avg_us": round(per_call_us[call], 2)}
 
     def bound_of(call):
