@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "rd_common.h"
 #include "rd_internal.h"
 
@@ -42,7 +44,6 @@ constexpr int kBlockN = 64;  // keys per tile
 constexpr int kCombRows = 64;  // rows per combine workgroup
 constexpr int kMaxSplits = 64;
 constexpr int kMaxMaskWords = (kMaxBeams * kMaxBeamLen) / 32;
-constexpr int kStages = 3;
 constexpr float kRescale = 8.f;  // lazy-rescale threshold of the online softmax (log2 units)
 
 struct AttnArgs {
@@ -75,7 +76,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4 *>(static_cast<uintptr_t>(addr)));
 }
 
-template <int D, int QPW, int NWAVE>
+template <int D, int QPW, int NWAVE, int KSPLIT, int NS>
 __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     constexpr int NKC = D / 32;              // k-steps over the head dim (QK^T)
     constexpr int NDB = D / 16;              // 16-row blocks of the head dim (PV)
@@ -86,10 +87,16 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     constexpr int KPL = 1024 / ROWB;         // keys per 1 KB load instruction
     constexpr int NT = 64 * NWAVE;           // threads per workgroup
     constexpr int NLD = kBlockN / KPL / NWAVE;  // load instructions per wavefront per operand per tile
-    constexpr int RB = NWAVE * QPW * 16;     // query rows per workgroup
+    constexpr int NQG = NWAVE / KSPLIT;      // query groups (wavefronts per key group)
+    constexpr int RB = NQG * QPW * 16;       // query rows per workgroup
+    constexpr int KW = kBlockN / KSPLIT;     // keys of a tile per key group
+    constexpr int NKB = KW / 16;             // 16-key blocks per key group
+    constexpr int NKS = KW / 32;             // 32-key PV steps per key group
     static_assert(NLD >= 1, "every wavefront issues loads");
     static_assert(KCH >= 8, "the swizzle permutes 8 chunks");
-    __shared__ __attribute__((aligned(1024))) uint8_t stage[kStages * STAGEB];
+    static_assert(QPW == 1 || QPW == 2, "one or two query blocks per wavefront");
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "a tile's keys go to one or two key groups");
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[NS * STAGEB];
     __shared__ uint32_t mwords[RB * kMaxMaskWords];  // tree-mask rows of this block's tokens
 
     // row blocks are the slowest index: blocks with no valid rows (their
@@ -103,6 +110,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wq = wave % NQG;  // query group
+    const int wk = wave / NQG;  // key group: keys wk*KW .. wk*KW+KW-1 of every tile
     const int lane = tid & 63;
     const int lq = lane & 15;
     const int kg = lane >> 4;
@@ -138,41 +147,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     }
     const int ntile = ncache + npk;
     const int tok_lo = row0 / a.G;
-
-    // this lane's query rows: block qi of wavefront w covers rows
-    // row0 + (NWAVE*qi + w)*16 .. +15 (interleaved, so few rows still
-    // spread over the wavefronts)
-    // A wavefront with at least one valid row multiplies all its blocks
-    // (padding rows hold zero queries); one with none only helps with the
-    // loads.  Valid rows form a prefix, so block 0 decides.
     bf16x8 qf[QPW][NKC];
     int lt[QPW];  // token of the row relative to tok_lo
-    const bool wave_active = row0 + wave * 16 < Mb;
-#pragma unroll
-    for (int qi = 0; qi < QPW; ++qi) {
-        const int r = row0 + (NWAVE * qi + wave) * 16 + lq;
-        const bool rvalid = r < Mb;
-        const int p = rvalid ? r / a.G : 0;
-        const int h = g * a.G + (rvalid ? r % a.G : 0);
-        lt[qi] = rvalid ? p - tok_lo : 0;
-        const uint16_t *qrow = a.q + ((static_cast<size_t>(b) * a.P + p) * a.Hq + h) * D;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            qf[qi][kc] = as_bf16x8(rvalid ? ld16(qrow + 32 * kc + 8 * kg) : make_uint4(0, 0, 0, 0));
-    }
-    // tokens of this block and their tree-mask rows, staged in LDS once
-    if (npk > 0) {
-        const int ntok = tok_hi - tok_lo;
-        const uint32_t *msrc = a.mask + (static_cast<size_t>(b) * a.P + tok_lo) * a.nw;
-        for (int i = tid; i < ntok * a.nw; i += NT) mwords[i] = msrc[i];
-    }
-    // The Q loads must land before the ring starts: at a first use inside
-    // the loop the compiler would wait for them -- and thereby for every ring
-    // load issued after them.
-#pragma unroll
-    for (int qi = 0; qi < QPW; ++qi)
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[qi][kc]));
+    int nact = 0;
 
     // K/V rows of tile i: cache tiles come first, then the packed tiles.
     // Keys past the valid range get an out-of-range offset and load zeros.
@@ -186,10 +163,13 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     const i32x4_t rv_n = make_srsrc(a.v_new + fresh_base, fresh_bytes);
     const uint32_t lds0 = lds_addr_of(stage);
 
-    // Cache tiles are visited from a per-block starting tile (wrapping) so
-    // that concurrent blocks, whose slabs sit at power-of-two strides, do
-    // not all address the same offsets and crowd a few HBM channels.
+    // Cache tile i holds the split's keys c0 + ic + ncache*j, j = 0..63
+    // (strided: the cache part of the softmax does not depend on key order,
+    // and strided tiles spread each load over many HBM pages instead of one
+    // 16 KB run), with ic rotated per block so that concurrent blocks, whose
+    // slabs sit at power-of-two strides, do not all address the same offsets.
     const int trot = ncache > 0 ? (b * 7 + g * 3 + qb * 5) % ncache : 0;
+    const int nck = c1 - c0;  // cache keys of this split
     // Load j = NWAVE*jj + wave of an operand covers tile keys KPL*j .. +KPL-1;
     // lane i stores LDS chunk slot i % KCH of key KPL*j + i / KCH, which
     // holds head-dim chunk slot ^ (key & 7).
@@ -200,7 +180,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         const i32x4_t rk = cache ? rk_c : rk_n;
         const i32x4_t rv = cache ? rv_c : rv_n;
         const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
-        const int kbase = cache ? c0 + ic * kBlockN : (i - ncache) * kBlockN;
+        const int kbase = cache ? c0 + ic : (i - ncache) * kBlockN;
+        const int kstep = cache ? ncache : 1;
         const int klim = (i >= ntile) ? 0 : (cache ? c1 : tok_hi);
         const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
         const uint32_t kdst = lds0 + slot * STAGEB;
@@ -208,7 +189,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         for (int jj = 0; jj < NLD; ++jj) {
             const int j = NWAVE * jj + wave;
             const int kl = KPL * j + lkey;
-            const int key = kbase + kl;
+            const int key = kbase + kstep * kl;
             const uint32_t off = key < klim ? static_cast<uint32_t>(key) * rowstride + ((lslot ^ (kl & 7)) << 4) : kOOB;
             lds_dma16(kdst + j * 1024, rk, off);
             lds_dma16(kdst + TILEB + j * 1024, rv, off);
@@ -241,67 +222,69 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         lpart[qi] = 0.f;
     }
 
-    // One pass over the tile for query blocks q0 .. q0+QG-1.
-    constexpr int QG = QPW < 2 ? QPW : 2;
-    auto compute_group = [&](int i, uint32_t sbase, int q0) {
+    // One pass over this key group's part of tile i for query blocks
+    // 0 .. NQ-1.  K fragments of a head-dim step are read one step ahead and
+    // serve every block; scores stay unscaled (the scale folds into the
+    // exponent).
+    auto compute_tile = [&](int i, uint32_t sbase, auto nq_c) {
+        constexpr int NQ = decltype(nq_c)::value;
         const uint8_t *st = stage + (sbase - lds0);
-        // S^T for 64 keys x 16 queries per block; the K fragments of a
-        // head-dim step are read once (one step ahead) for all blocks of the
-        // pass.  Scores stay unscaled: the scale folds into the exponent.
-        f32x4 sc[QG][4];
+        f32x4 sc[NQ][NKB];
 #pragma unroll
-        for (int qi = 0; qi < QG; ++qi)
+        for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sc[qi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 ka[2][4];
+            for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t kgrp = wk * NKB * 16 * ROWB;
+        bf16x8 ka[2][NKB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ka[0][kb] = *reinterpret_cast<const bf16x8 *>(st + koff[0] + kb * 16 * ROWB);
+        for (int kb = 0; kb < NKB; ++kb)
+            ka[0][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[0] + kb * 16 * ROWB);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             if (kc + 1 < NKC)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    ka[(kc + 1) & 1][kb] = *reinterpret_cast<const bf16x8 *>(st + koff[kc + 1] + kb * 16 * ROWB);
+                for (int kb = 0; kb < NKB; ++kb)
+                    ka[(kc + 1) & 1][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[kc + 1] + kb * 16 * ROWB);
 #pragma unroll
-            for (int qi = 0; qi < QG; ++qi)
+            for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[q0 + qi][kc], sc[qi][kb]);
+                for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[qi][kc], sc[qi][kb]);
         }
 
         // mask (partial cache tiles and packed tiles only), online softmax;
-        // key of sc[qi][kb][e] within the tile is kb*16 + 4*kg + e
+        // key of sc[qi][kb][e] within the tile is (wk*NKB + kb)*16 + 4*kg + e
+        // cache key j of the tile is valid iff ic + ncache*j < nck; packed
+        // key j iff j < lim and its mask bit is set
         const bool cache = i < ncache;
         const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
-        const int lim = cache ? c1 - (c0 + ic * kBlockN) : tok_hi - (i - ncache) * kBlockN;
-        const bool full = cache && lim >= kBlockN;  // wave-uniform
+        const int lim = cache ? nck : tok_hi - (i - ncache) * kBlockN;
+        const bool full = cache && ic + ncache * (kBlockN - 1) < nck;  // wave-uniform
         const int wi = 2 * (i - ncache);
         if (!full) {
 #pragma unroll
-            for (int qi = 0; qi < QG; ++qi) {
+            for (int qi = 0; qi < NQ; ++qi) {
                 uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
                 if (!cache) {
-                    w0 = mwords[lt[q0 + qi] * a.nw + wi];
-                    w1 = (wi + 1 < a.nw) ? mwords[lt[q0 + qi] * a.nw + wi + 1] : 0u;
+                    w0 = mwords[lt[qi] * a.nw + wi];
+                    w1 = (wi + 1 < a.nw) ? mwords[lt[qi] * a.nw + wi + 1] : 0u;
                 }
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int j = kb * 16 + 4 * kg + e;
+                        const int j = (wk * NKB + kb) * 16 + 4 * kg + e;
                         const uint32_t wd = (j < 32) ? w0 : w1;
-                        const bool vis = (j < lim) && ((wd >> (j & 31)) & 1u);
+                        const bool vis = cache ? (ic + ncache * j < lim) : ((j < lim) && ((wd >> (j & 31)) & 1u));
                         sc[qi][kb][e] = vis ? sc[qi][kb][e] : -INFINITY;
                     }
             }
         }
-        bf16x8 pb[QG][2];
+        bf16x8 pb[NQ][NKS];
 #pragma unroll
-        for (int qi = 0; qi < QG; ++qi) {
-            const int q = q0 + qi;
+        for (int qi = 0; qi < NQ; ++qi) {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[qi][kb][e]);
             tmax = fmaxf(tmax, shfl_xor(tmax, 16));
@@ -312,28 +295,28 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             // in registers untouched on most tiles.  Exact: O and l are both
             // taken relative to the same reference, and probabilities stay
             // below 2^kRescale.
-            if (__any(tmax > mrun[q] + kRescale)) {
-                const float mnew = fmaxf(mrun[q], tmax);
-                const float alpha = fast_exp2(mrun[q] - mnew);
-                mrun[q] = mnew;
-                lpart[q] *= alpha;
+            if (__any(tmax > mrun[qi] + kRescale)) {
+                const float mnew = fmaxf(mrun[qi], tmax);
+                const float alpha = fast_exp2(mrun[qi] - mnew);
+                mrun[qi] = mnew;
+                lpart[qi] *= alpha;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[q][db] *= alpha;
+                for (int db = 0; db < NDB; ++db) o[qi][db] *= alpha;
             }
-            const float mref = mrun[q];
+            const float mref = mrun[qi];
             float psum = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     sc[qi][kb][e] = fast_exp2(fmaf(sc[qi][kb][e], a.scale_log2, -mref));
                     psum += sc[qi][kb][e];
                 }
-            lpart[q] += psum;
-            // P^T as the B operand of the two 32-key steps: slots 0-3 hold
-            // keys 32*ks + 4*kg + (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
+            lpart[qi] += psum;
+            // P^T as the B operand of the 32-key steps: slots 0-3 hold keys
+            // 32*ks + 4*kg + (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     pb[qi][ks][e] = static_cast<__bf16>(sc[qi][2 * ks][e]);
@@ -341,14 +324,13 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                 }
         }
 
-        // O^T += V^T P^T over 2*NDB steps (ks, db); each V^T fragment (two
-        // transpose loads) serves every block of the pass and is read kVPre
-        // steps ahead
-        constexpr int NSTEP = 2 * NDB;
+        // O^T += V^T P^T over NKS*NDB steps (ks, db); each V^T fragment (two
+        // transpose loads) serves every block and is read kVPre steps ahead
+        constexpr int NSTEP = NKS * NDB;
         constexpr int kVPre = 4;
         auto vaddr = [&](int n) {
             const int ks = n / NDB, db = n % NDB;
-            return sbase + voff[db & 3] + (db >> 2) * 128 + ks * 32 * ROWB;
+            return sbase + voff[db & 3] + (db >> 2) * 128 + (wk * NKS + ks) * 32 * ROWB;
         };
         bf16x4 vlo[kVPre], vhi[kVPre];
 #pragma unroll
@@ -370,44 +352,119 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             }
             const int ks = n / NDB, db = n % NDB;
 #pragma unroll
-            for (int qi = 0; qi < QG; ++qi) o[q0 + qi][db] = mfma16x16x32(vf, pb[qi][ks], o[q0 + qi][db]);
+            for (int qi = 0; qi < NQ; ++qi) o[qi][db] = mfma16x16x32(vf, pb[qi][ks], o[qi][db]);
         }
     };
-    auto compute_tile = [&](int i, uint32_t sbase) {
-#pragma unroll
-        for (int q0 = 0; q0 < QPW; q0 += QG) compute_group(i, sbase, q0);
-    };
 
-    // Ring of kStages LDS stages.  Tiles 0..kStages-2 are issued up front.
+    // Ring of NS LDS stages.  Tiles 0..NS-2 are issued up front.
     // At the top of tile i this wavefront's loads of tile i have landed once
-    // at most (kStages-2)*2*NLD of its loads remain outstanding; the barrier
+    // at most (NS-2)*2*NLD of its loads remain outstanding; the barrier
     // publishes every wavefront's share and certifies that all reads of the
-    // slot of tile i-1 are done, so tile i+kStages-1 may be loaded into it.
+    // slot of tile i-1 are done, so tile i+NS-1 may be loaded into it.
     // Tiles past the last still issue their loads, all out of range, so
     // every wait counts the same number of loads.
 #pragma unroll
-    for (int st = 0; st < kStages - 1; ++st) issue_tile(st, st);
-    int cslot = 0, lslot_ring = kStages - 1;  // slots of the tile computed / loaded
+    for (int st = 0; st < NS - 1; ++st) issue_tile(st, st);
+    // this lane's query rows: block qi of query group q covers rows
+    // row0 + (NQG*qi + q)*16 .. +15 (interleaved, so few rows still spread
+    // over the groups).  Valid blocks form a prefix in qi; a wavefront
+    // multiplies only its valid ones (none: it only helps with the loads).
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+        const int rbase = row0 + (NQG * qi + wq) * 16;
+        nact += (rbase < Mb) ? 1 : 0;
+        const int r = rbase + lq;
+        const bool rvalid = r < Mb;
+        const int p = rvalid ? r / a.G : 0;
+        const int h = g * a.G + (rvalid ? r % a.G : 0);
+        lt[qi] = rvalid ? p - tok_lo : 0;
+        const uint16_t *qrow = a.q + ((static_cast<size_t>(b) * a.P + p) * a.Hq + h) * D;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+            qf[qi][kc] = as_bf16x8(rvalid ? ld16(qrow + 32 * kc + 8 * kg) : make_uint4(0, 0, 0, 0));
+    }
+    nact = __builtin_amdgcn_readfirstlane(nact);
+    // tokens of this block and their tree-mask rows, staged in LDS once
+    if (npk > 0) {
+        const int ntok = tok_hi - tok_lo;
+        const uint32_t *msrc = a.mask + (static_cast<size_t>(b) * a.P + tok_lo) * a.nw;
+        for (int i = tid; i < ntok * a.nw; i += NT) mwords[i] = msrc[i];
+    }
+    // The Q and mask loads are issued after the ring's first tiles, so
+    // their latency overlaps that of the ring; at a first use inside the
+    // loop the compiler would wait for them (and for all earlier loads), so
+    // they are made to land here, where that wait costs nothing extra.
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[qi][kc]));
+
+    int cslot = 0, lslot_ring = NS - 1;  // slots of the tile computed / loaded
     for (int i = 0; i < ntile; ++i) {
-        vm_wait<(kStages - 2) * 2 * NLD>();
+        vm_wait<(NS - 2) * 2 * NLD>();
         __syncthreads();
-        issue_tile(i + kStages - 1, lslot_ring);
-        if (wave_active) compute_tile(i, lds0 + cslot * STAGEB);
-        cslot = (cslot + 1 == kStages) ? 0 : cslot + 1;
-        lslot_ring = (lslot_ring + 1 == kStages) ? 0 : lslot_ring + 1;
+        issue_tile(i + NS - 1, lslot_ring);
+        const uint32_t sbase = lds0 + cslot * STAGEB;
+        if (QPW == 2 && nact == 2)
+            compute_tile(i, sbase, std::integral_constant<int, QPW>{});
+        else if (nact >= 1)
+            compute_tile(i, sbase, std::integral_constant<int, 1>{});
+        cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
+        lslot_ring = (lslot_ring + 1 == NS) ? 0 : lslot_ring + 1;
     }
     vm_wait<0>();
 
+    // per-row sums over the four k-groups of the lane's column
+    float lsum[QPW];
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
-        float lsum = lpart[qi] + shfl_xor(lpart[qi], 16);
-        lsum += shfl_xor(lsum, 32);
-        const int r = row0 + (NWAVE * qi + wave) * 16 + lq;
+        lsum[qi] = lpart[qi] + shfl_xor(lpart[qi], 16);
+        lsum[qi] += shfl_xor(lsum[qi], 32);
+    }
+    if (KSPLIT == 2) {
+        // key group 1 hands (m, l, O) to key group 0 through LDS (the ring is
+        // drained), which merges: M = max(m0, m1), O = O0 2^(m0-M) + O1 2^(m1-M)
+        __syncthreads();
+        float *xo = reinterpret_cast<float *>(stage);                  // [NQG][QPW][NDB][64] f32x4
+        float *xm = xo + NQG * QPW * NDB * 64 * 4;                      // [NQG][QPW][64] m, l
+        if (wk == 1) {
+#pragma unroll
+            for (int qi = 0; qi < QPW; ++qi) {
+                if (qi >= nact) break;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    *reinterpret_cast<f32x4 *>(xo + (((wq * QPW + qi) * NDB + db) * 64 + lane) * 4) = o[qi][db];
+                xm[((wq * QPW + qi) * 64 + lane) * 2] = mrun[qi];
+                xm[((wq * QPW + qi) * 64 + lane) * 2 + 1] = lsum[qi];
+            }
+        }
+        __syncthreads();
+        if (wk == 1) return;
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) {
+            if (qi >= nact) break;
+            const float m1 = xm[((wq * QPW + qi) * 64 + lane) * 2];
+            const float l1 = xm[((wq * QPW + qi) * 64 + lane) * 2 + 1];
+            const float M = fmaxf(mrun[qi], m1);
+            const float a0 = fast_exp2(mrun[qi] - M), a1 = fast_exp2(m1 - M);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const f32x4 o1 = *reinterpret_cast<const f32x4 *>(xo + (((wq * QPW + qi) * NDB + db) * 64 + lane) * 4);
+                o[qi][db] = o[qi][db] * a0 + o1 * a1;
+            }
+            mrun[qi] = M;
+            lsum[qi] = lsum[qi] * a0 + l1 * a1;
+        }
+    }
+
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+        const int r = row0 + (NQG * qi + wq) * 16 + lq;
         const bool rvalid = r < Mb;
         if (a.nsplit == 1) {
             // o[qi][db][e] = O[query r][d = db*16 + 4*kg + e]; padding rows get zeros
             if (r < Mpad) {
-                const float inv = (rvalid && lsum > 0.f) ? 1.f / lsum : 0.f;
+                const float inv = (rvalid && lsum[qi] > 0.f) ? 1.f / lsum[qi] : 0.f;
                 const int pz = r / a.G, hz = g * a.G + r % a.G;
                 uint16_t *orow = a.out + ((static_cast<size_t>(b) * a.P + pz) * a.Hq + hz) * D;
 #pragma unroll
@@ -422,7 +479,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             float *orow = a.ws_o + prow * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4 *>(orow + db * 16 + 4 * kg) = o[qi][db];
-            if (kg == 0) a.ws_ml[prow] = make_float2(mrun[qi], lsum);
+            if (kg == 0) a.ws_ml[prow] = make_float2(mrun[qi], lsum[qi]);
         }
     }
 }
@@ -567,16 +624,20 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max) {
-    AttnPlan plan{0, 1, kBlockN, 0, 1, 0, 4};
+    AttnPlan plan{0, 1, kBlockN, 0, 1, 0, 4, 1};
     if (dtype != 1) return plan;  // fp32 path needs no workspace
     const int G = Hq / Hkv;
     const int rows = G * P_max;
     // 16-row query blocks per wavefront: enough that one workgroup holds all
     // rows of a (request, KV head) whenever they fit in 256
-    // (QPW, wavefronts) = (1, 4), (2, 4) or (2, 8): 64, 128 or 256 rows
-    plan.qpw = rows <= 64 ? 1 : 2;
+    // (QPW, wavefronts, key groups): up to 64 rows (2, 4, 2) -- two
+    // query groups, each tile's keys split over two wavefronts, so all four
+    // SIMDs work even for a handful of rows; up to 128 rows (2, 4, 1);
+    // more (2, 8, 1) = 256 rows per workgroup
+    plan.qpw = 2;
     plan.nwave = rows <= 128 ? 4 : 8;
-    const int rb = 16 * plan.qpw * plan.nwave;
+    plan.ksplit = rows <= 64 ? 2 : 1;
+    const int rb = 16 * plan.qpw * plan.nwave / plan.ksplit;
     plan.nqblk = (rows + rb - 1) / rb;
     plan.rows_unit = plan.nqblk * rb;
     // One workgroup per CU fits (the LDS ring): split the cache only as far
@@ -642,14 +703,16 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
     a.ws_ml = (plan.nsplit > 1) ? reinterpret_cast<float2 *>(static_cast<float *>(ws) + nrow * D) : nullptr;
     const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * Hkv * plan.nsplit * plan.nqblk));
     const dim3 blk(64 * plan.nwave);
+    // ring depth: three stages (measured on MI355X: two starve the MFMA-heavy
+    // shapes, four did not stream faster)
     if (D == 64) {
-        if (plan.qpw == 1) hipLaunchKernelGGL((k_tree_attn_bf16<64, 1, 4>), grid, blk, 0, stream, a);
-        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4>), grid, blk, 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 8>), grid, blk, 0, stream, a);
+        if (plan.ksplit == 2) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4, 2, 3>), grid, blk, 0, stream, a);
+        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4, 1, 3>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 8, 1, 3>), grid, blk, 0, stream, a);
     } else {
-        if (plan.qpw == 1) hipLaunchKernelGGL((k_tree_attn_bf16<128, 1, 4>), grid, blk, 0, stream, a);
-        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4>), grid, blk, 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 8>), grid, blk, 0, stream, a);
+        if (plan.ksplit == 2) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4, 2, 3>), grid, blk, 0, stream, a);
+        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4, 1, 3>), grid, blk, 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 8, 1, 3>), grid, blk, 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || plan.nsplit == 1) return err;

@@ -25,6 +25,7 @@ struct AttnPlan {
     int qpw;        // 16-row query blocks per wavefront (1 or 2)
     int rows_unit;  // nqblk * rows per workgroup
     int nwave;      // wavefronts per workgroup (4 or 8)
+    int ksplit;     // wavefronts sharing one query block's keys of a tile (1 or 2)
 };
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max);
 hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *k_new,
