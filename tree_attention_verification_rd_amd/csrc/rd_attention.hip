@@ -163,13 +163,18 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     const i32x4_t rv_n = make_srsrc(a.v_new + fresh_base, fresh_bytes);
     const uint32_t lds0 = lds_addr_of(stage);
 
-    // Cache tile i holds the split's keys c0 + ic + ncache*j, j = 0..63
-    // (strided: the cache part of the softmax does not depend on key order,
-    // and strided tiles spread each load over many HBM pages instead of one
-    // 16 KB run), with ic rotated per block so that concurrent blocks, whose
-    // slabs sit at power-of-two strides, do not all address the same offsets.
+    // Cache tile i holds the split's keys c0 + pos(j), j = 0..63, with
+    // pos(j) = ic*64 + j, or, on the split-KV path, the strided ic + ncache*j
+    // (the cache part of the softmax does not depend on key order; strided
+    // tiles spread each load of a long cache over many HBM pages instead of
+    // one 16 KB run, which measured faster there and slower elsewhere).  ic
+    // is rotated per block so that concurrent blocks, whose slabs sit at
+    // power-of-two strides, do not all address the same offsets.
     const int trot = ncache > 0 ? (b * 7 + g * 3 + qb * 5) % ncache : 0;
     const int nck = c1 - c0;  // cache keys of this split
+    const bool strided = a.nsplit > 1;
+    const int kmul = strided ? ncache : 1;  // pos(j) = ic*kblk + kmul*j
+    const int kblk = strided ? 1 : kBlockN;
     // Load j = NWAVE*jj + wave of an operand covers tile keys KPL*j .. +KPL-1;
     // lane i stores LDS chunk slot i % KCH of key KPL*j + i / KCH, which
     // holds head-dim chunk slot ^ (key & 7).
@@ -180,8 +185,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         const i32x4_t rk = cache ? rk_c : rk_n;
         const i32x4_t rv = cache ? rv_c : rv_n;
         const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
-        const int kbase = cache ? c0 + ic : (i - ncache) * kBlockN;
-        const int kstep = cache ? ncache : 1;
+        const int kbase = cache ? c0 + ic * kblk : (i - ncache) * kBlockN;
+        const int kstep = cache ? kmul : 1;
         const int klim = (i >= ntile) ? 0 : (cache ? c1 : tok_hi);
         const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
         const uint32_t kdst = lds0 + slot * STAGEB;
@@ -253,12 +258,12 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
 
         // mask (partial cache tiles and packed tiles only), online softmax;
         // key of sc[qi][kb][e] within the tile is (wk*NKB + kb)*16 + 4*kg + e
-        // cache key j of the tile is valid iff ic + ncache*j < nck; packed
-        // key j iff j < lim and its mask bit is set
+        // cache key j of the tile is valid iff pos(j) < nck; packed key j
+        // iff j < lim and its mask bit is set
         const bool cache = i < ncache;
         const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
         const int lim = cache ? nck : tok_hi - (i - ncache) * kBlockN;
-        const bool full = cache && ic + ncache * (kBlockN - 1) < nck;  // wave-uniform
+        const bool full = cache && ic * kblk + kmul * (kBlockN - 1) < nck;  // wave-uniform
         const int wi = 2 * (i - ncache);
         if (!full) {
 #pragma unroll
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                     for (int e = 0; e < 4; ++e) {
                         const int j = (wk * NKB + kb) * 16 + 4 * kg + e;
                         const uint32_t wd = (j < 32) ? w0 : w1;
-                        const bool vis = cache ? (ic + ncache * j < lim) : ((j < lim) && ((wd >> (j & 31)) & 1u));
+                        const bool vis = cache ? (ic * kblk + kmul * j < lim) : ((j < lim) && ((wd >> (j & 31)) & 1u));
                         sc[qi][kb][e] = vis ? sc[qi][kb][e] : -INFINITY;
                     }
             }

@@ -101,10 +101,10 @@ __device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32
     }
 }
 
-template <int WV, int WR, int GV, int GR, int NS, int BK>
+template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK>
 __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     static_assert(GV * GR == 4, "four wavefronts per workgroup");
-    static_assert(NS >= 2, "the ring needs a stage in flight while another is consumed");
+    static_assert(NSX >= 2 && NSW >= NSX, "each ring needs a stage in flight while another is consumed");
     static_assert(BK == 32 || BK == 64, "one or two 32-wide MFMA steps per k-step");
     constexpr int NSUB = BK / 32;            // MFMA k-steps per staged k-step
     constexpr int BV = GV * WV;              // vocabulary rows per tile
@@ -114,13 +114,14 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     constexpr int kRowB = BK * 2;            // bytes of one staged row (a cache line or half of one)
     constexpr int CPR = BK / 8;              // 16-byte chunks per staged row
     constexpr int RPL = 1024 / kRowB;        // rows per 1 KB load instruction
-    constexpr int kStageRows = BV + BR;
-    constexpr int kStageBytes = kStageRows * kRowB;
-    constexpr int NL = kStageRows / RPL / 4; // LDS loads per wavefront per stage
+    constexpr int kWStage = BV * kRowB;      // bytes of one weight stage
+    constexpr int kXStage = BR * kRowB;      // bytes of one hidden stage
+    constexpr int kXBase = NSW * kWStage;    // hidden ring after the weight ring
+    constexpr int NL = (BV + BR) / RPL / 4;  // LDS loads per wavefront per k-step (both operands)
     constexpr int NLW = BV / RPL / 4;        // ... of weight rows
     constexpr int NLX = BR / RPL / 4;        // ... of hidden rows
     static_assert(BV % (4 * RPL) == 0 && BR % (4 * RPL) == 0, "each wavefront loads whole groups of both operands");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSW * kWStage + NSX * kXStage];
     __shared__ int32_t rmap[BR];  // packed row (b*P + p) of each compact row of the tile
     __shared__ int scan_tmp[4];
 
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     // with chunk bit 2 flipped
     const uint32_t sw = static_cast<uint32_t>((kg ^ swz(lq)) << 4);
     const uint32_t aoff = static_cast<uint32_t>(gv * WV + lq) * kRowB + sw;
-    const uint32_t boff = static_cast<uint32_t>(BV + gr * WR + lq) * kRowB + sw;
+    const uint32_t boff = static_cast<uint32_t>(gr * WR + lq) * kRowB + sw;
     // All workgroups on one XCD (block i runs on XCD i % 8) walk K in the
     // same order and mostly run side by side, so the rows they share are
     // fetched into that XCD's L2 once; the XCDs start at different k-steps
@@ -196,23 +197,33 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         uint32_t xbase[NLX];
 #pragma unroll
         for (int i = 0; i < NLX; ++i) {
-            const int m = r0 + RPL * (4 * (NLW + i) + wave) + lrow - BV;
+            const int m = r0 + RPL * (4 * i + wave) + lrow;
             xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
         }
-        // Stage kt (k-step (kt + krot) mod nk) goes to ring slot kt % NS.
+        // The weight rows of k-step kt (k-step (kt + krot) mod nk) go to
+        // weight-ring slot kt % NSW, its hidden rows to hidden-ring slot
+        // kt % NSX.  The weight stream comes from HBM and is issued NSW-1
+        // k-steps ahead; the hidden rows are L2 hits and need less lead.
         // Stages past the last k-step still issue their loads, all out of
         // range (zeros), so every wait below counts the same number of loads.
-        auto issue_stage = [&](int kt, int slot) {
-            const int kr = (kt < nk) ? ((kt + krot >= nk) ? kt + krot - nk : kt + krot) : -1;
+        auto kstep_of = [&](int kt) { return (kt < nk) ? ((kt + krot >= nk) ? kt + krot - nk : kt + krot) : -1; };
+        auto issue_w = [&](int kt, int slot) {
+            const int kr = kstep_of(kt);
             const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
             const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
-            const uint32_t sbase = lds0 + slot * kStageBytes + wave * 1024;
+            const uint32_t sbase = lds0 + slot * kWStage + wave * 1024;
 #pragma unroll
             for (int i = 0; i < NLW; ++i)
                 lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 4 * RPL * rowb + kadd : kOOB);
+        };
+        auto issue_x = [&](int kt, int slot) {
+            const int kr = kstep_of(kt);
+            const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
+            const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
+            const uint32_t sbase = lds0 + kXBase + slot * kXStage + wave * 1024;
 #pragma unroll
             for (int i = 0; i < NLX; ++i)
-                lds_dma16(sbase + (NLW + i) * 4096, xres, kin ? xbase[i] + kadd : kOOB);
+                lds_dma16(sbase + i * 4096, xres, kin ? xbase[i] + kadd : kOOB);
         };
         // a wavefront whose rows are all padding only helps with the loads
         const bool active = r0 + gr * WR < R;
@@ -223,12 +234,15 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // Ring of NS LDS stages.  Stages 0..NS-2 are issued up front.  At
-        // the top of k-step kt this wavefront's loads of stage kt have landed
-        // once at most (NS-2)*NL of its loads remain outstanding; the barrier
-        // then publishes every wavefront's share and also certifies that all
-        // reads of slot (kt-1) % NS are done, so stage kt+NS-1 may be loaded
-        // into it.
+        // Two LDS rings.  Issue order is: weight stages 0..NSW-NSX-1 alone,
+        // then pairs (weight stage j + NSW - NSX, hidden stage j) for j = 0,
+        // 1, ...; k-step kt issues the pair with j = kt + NSX - 1.  At the top
+        // of k-step kt this wavefront's hidden loads of stage kt -- and so,
+        // loads completing in order, its earlier weight loads of stage kt --
+        // have landed once at most (NSX-2) pairs remain outstanding; the
+        // barrier then publishes every wavefront's share and certifies that
+        // all reads of the slots of k-step kt-1 are done, so they may be
+        // reloaded.
         //
         // Fragments are software-pipelined across the barrier: the last
         // 32-wide MFMA step of k-step kt is read into registers before the
@@ -237,13 +251,14 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         // the MFMAs.  (The first k-step multiplies zero fragments in that
         // slot.)  With one MFMA step per k-step the two fragment buffers
         // alternate between k-steps.
-        auto read_frags = [&](const uint8_t *st, uint32_t x, bf16x8 (&fa)[NVB], bf16x8 (&fb)[NRB]) {
+        auto read_frags = [&](const uint8_t *wst, const uint8_t *xst, uint32_t x, bf16x8 (&fa)[NVB],
+                              bf16x8 (&fb)[NRB]) {
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb)
-                fa[vb] = *reinterpret_cast<const bf16x8 *>(st + ((aoff ^ x) + vb * 16 * kRowB));
+                fa[vb] = *reinterpret_cast<const bf16x8 *>(wst + ((aoff ^ x) + vb * 16 * kRowB));
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
-                fb[rb] = *reinterpret_cast<const bf16x8 *>(st + ((boff ^ x) + rb * 16 * kRowB));
+                fb[rb] = *reinterpret_cast<const bf16x8 *>(xst + ((boff ^ x) + rb * 16 * kRowB));
         };
         auto mma = [&](const bf16x8 (&fa)[NVB], const bf16x8 (&fb)[NRB]) {
 #pragma unroll
@@ -258,23 +273,29 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         for (int rb = 0; rb < NRB; ++rb) fb2[1][rb] = bf16x8{};
 
 #pragma unroll
-        for (int s = 0; s < NS - 1; ++s) issue_stage(s, s);
+        for (int s = 0; s < NSW - NSX; ++s) issue_w(s, s);
+#pragma unroll
+        for (int j = 0; j < NSX - 1; ++j) {
+            issue_w(j + NSW - NSX, j + NSW - NSX);
+            issue_x(j, j);
+        }
 
         // The k loop is unrolled by two (the fragment buffers alternate);
         // ring slots are tracked at run time.
-        int cslot = 0;  // slot of k-step kt
+        int wslot = 0, xslot = 0;  // slots of k-step kt
         auto step = [&](int kt, auto cur_c) {
             constexpr int cur = decltype(cur_c)::value;  // fragment buffer of this k-step
-            vm_wait<(NS - 2) * NL>();
+            vm_wait<(NSX - 2) * NL>();
             __syncthreads();
-            const int lslot = (cslot == 0) ? NS - 1 : cslot - 1;  // (kt + NS - 1) % NS
-            issue_stage(kt + NS - 1, lslot);
+            issue_w(kt + NSW - 1, (wslot == 0) ? NSW - 1 : wslot - 1);  // slot (kt + NSW - 1) % NSW
+            issue_x(kt + NSX - 1, (xslot == 0) ? NSX - 1 : xslot - 1);
             if (active) {
-                const uint8_t *st = lds + cslot * kStageBytes;
+                const uint8_t *wst = lds + wslot * kWStage;
+                const uint8_t *xst = lds + kXBase + xslot * kXStage;
                 if constexpr (NSUB == 2) {
-                    read_frags(st, 0u, fa2[0], fb2[0]);
+                    read_frags(wst, xst, 0u, fa2[0], fb2[0]);
                     mma(fa2[1], fb2[1]);
-                    read_frags(st, 64u, fa2[1], fb2[1]);
+                    read_frags(wst, xst, 64u, fa2[1], fb2[1]);
                     mma(fa2[0], fb2[0]);
                     // keep that order: reads, multiplies, reads, multiplies
                     __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
@@ -282,13 +303,14 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
                     __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
                 } else {
-                    read_frags(st, 0u, fa2[cur], fb2[cur]);
+                    read_frags(wst, xst, 0u, fa2[cur], fb2[cur]);
                     mma(fa2[cur ^ 1], fb2[cur ^ 1]);
                     __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
                 }
             }
-            cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
+            wslot = (wslot + 1 == NSW) ? 0 : wslot + 1;
+            xslot = (xslot + 1 == NSX) ? 0 : xslot + 1;
         };
         // An odd k-step count gets one padding step (its loads are out of
         // range, so it multiplies zeros); the held buffer is then always [1].
@@ -473,10 +495,13 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
         plan.variant = 0;
     } else {
         // Two tile shapes.  Few rows (the weight stream dominates): 128
-        // vocabulary x 256 rows per tile, 128x64 per wavefront, three-stage
-        // ring -- twice as many tiles to spread over the CUs.  Many rows (the
-        // MFMAs dominate): 256 x 256 per tile, 128x128 per wavefront, two
-        // stages -- a third less L2 traffic per flop.  RD_LM_VARIANT forces one.
+        // vocabulary x 256 rows per tile, 128x64 per wavefront, k-steps of
+        // 64, three weight and three hidden stages -- twice as many tiles to
+        // spread over the CUs.  Many rows (the MFMAs dominate): 256 x 256 per
+        // tile, 128x128 per wavefront, k-steps of 32, five weight and four
+        // hidden stages -- a third less L2 traffic per flop.  (Ring depths
+        // measured on MI355X: deeper weight rings slow the few-row shape.)
+        // RD_LM_VARIANT forces one.
         const char *env = getenv("RD_LM_VARIANT");
         plan.variant = (env && *env) ? (atoi(env) != 0) : (plan.rows_pad > 512 ? 1 : 0);
         plan.vtile = plan.variant ? 256 : 128;
@@ -516,9 +541,9 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.nrt = static_cast<int>((rows + plan.rtile - 1) / plan.rtile);
         const dim3 grid(static_cast<unsigned>(a.nrt * a.nvt));
         if (plan.variant == 0)
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 64>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 4, 32>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32>), grid, dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
