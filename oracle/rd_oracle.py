@@ -27,7 +27,12 @@ Pinned by tests that do not reuse this file's formulas: brute-force prefix
 counting, exhaustive tiny beam sets, a PyTorch gather restating the pages'
 unpack, PyTorch scaled-dot-product attention on single-beam trees, closed
 forms (self-only attention, uniform scores, one-hot projections), GQA versus
-repeated-head MHA, and hand-worked accept cases under tests/golden/.
+repeated-head MHA, and hand-worked accept cases under tests/golden/.  The
+commit of the accepted path is pinned by decoding over the committed cache
+(torch scaled-dot-product attention must reproduce verification's output
+for every accepted candidate), by the committed rows spelling the text that
+the greedy accept reports, and by the chosen hidden state re-deriving the
+bonus token.
 """
 from __future__ import annotations
 
@@ -38,7 +43,7 @@ import numpy as np
 __all__ = [
     "pack_beams", "tree_mask", "mask_to_bits", "attention_per_beam",
     "attention_packed", "lm_head_logits", "argmax_first", "unpack",
-    "greedy_accept", "verify_requests",
+    "greedy_accept", "commit_accepted", "verify_requests",
 ]
 
 
@@ -273,6 +278,54 @@ def greedy_accept(beams: np.ndarray, target: np.ndarray) -> dict:
         accepted[b, :len(toks)] = toks
     return {"match_len": match_len, "best_beam": best_beam, "accept_len": accept_len,
             "accepted_tokens": accepted}
+
+
+# ------------------------------------------------------- after step 4 --
+def commit_accepted(k, v, hidden, best_beam, accept_len, k_cache, v_cache, kv_len) -> dict:
+    """Append the accepted path to the KV cache; pick the drafter's hidden state.
+
+    [TRT] intro: the best path is accepted before the next drafting round,
+    so its tokens join the context the next step attends to.  [NEWS] "RNN
+    draft model": the drafter continues from the target's latest token and
+    the target's last hidden state.
+
+    Reading (the pages name the step, not its data movement): with
+    w = best_beam[b] and n = accept_len[b], candidates (b,w,0..n) are the
+    target's initial token and the n accepted drafts.  Their keys and values
+    were computed during verification over exactly the context plain
+    decoding gives them (the beam's own prefix plus the cache), so they are
+    appended in order at positions kv_len[b] .. kv_len[b]+n of every KV head
+    and kv_len[b] grows by n+1.  The bonus token has no key or value yet; it
+    opens the next step's beams.  hidden_next[b] is the hidden state of
+    candidate (b,w,n), whose logits chose the bonus token.  A request whose
+    best_beam or accept_len is out of range, or whose appended rows would
+    pass the cache capacity S, is left unchanged (committed[b] False,
+    hidden_next[b] NaN): the pages say nothing about overflow.
+
+    k, v [B,W,L,Hkv,D] and hidden [B,W,L,K] are per candidate (the unpacked
+    definition); k_cache, v_cache [B,Hkv,S,D]; kv_len [B].  Returns fp64
+    copies of the caches, int32 kv_len, bool committed [B], fp64
+    hidden_next [B,K].
+    """
+    B, W, L = np.asarray(k).shape[:3]
+    S = k_cache.shape[2]
+    kc = np.array(k_cache, np.float64)
+    vc = np.array(v_cache, np.float64)
+    new_len = np.array(kv_len, np.int32)
+    committed = np.zeros(B, bool)
+    hidden_next = np.full((B, np.asarray(hidden).shape[3]), np.nan)
+    for b in range(B):
+        w, n, c = int(best_beam[b]), int(accept_len[b]), int(kv_len[b])
+        if not (0 <= w < W and 0 <= n <= L - 1 and 0 <= c and c + n + 1 <= S):
+            continue
+        for j in range(n + 1):
+            kc[b, :, c + j] = k[b, w, j]          # every KV head at once: [Hkv, D]
+            vc[b, :, c + j] = v[b, w, j]
+        new_len[b] = c + n + 1
+        committed[b] = True
+        hidden_next[b] = hidden[b, w, n]
+    return {"k_cache": kc, "v_cache": vc, "kv_len": new_len, "committed": committed,
+            "hidden_next": hidden_next}
 
 
 # ------------------------------------------------------------- the step --
