@@ -224,6 +224,46 @@ def main():
     names = ["pack", "mask", "attention", "lm_head", "unpack_accept"]
     per_call_us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]) * 1e3) for j, n in enumerate(names)}
 
+    # The commit of the accepted path, the call after the step (not part of
+    # the timed step): timed alone, at full acceptance (n = L-1 on beam 0) so
+    # every request appends L rows per KV head.  Call i advances its own
+    # kv_len row, so no reset runs between calls.  The kernel is shorter than
+    # its host-side enqueue, so a busy-wait kernel sized to the measured
+    # enqueue time goes first: the calls then run back to back and the
+    # events time the GPU, not the host.
+    c_best = torch.zeros(B, dtype=torch.int32, device=dev)
+    c_nacc = torch.full((B,), cfg.L - 1, dtype=torch.int32, device=dev)
+    c_kv = torch.empty((K, B), dtype=torch.int32, device=dev)
+    c_hid = torch.empty((B, cfg.hidden), dtype=dt, device=dev)
+    c_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+
+    def commit_pass():
+        for i in range(K):
+            s = sets[i % n_sets]
+            c_evs[i][0].record()
+            rd.rd_commit_accepted(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], s["k_cache"],
+                                  s["v_cache"], c_kv[i], s["hidden"], hidden_next=c_hid)
+            c_evs[i][1].record()
+
+    c_kv.fill_(cfg.S - cfg.L)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    commit_pass()
+    enqueue_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    cal = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cal[0].record()
+    torch.cuda._sleep(1_000_000)
+    cal[1].record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(cal[0].elapsed_time(cal[1]), 1e-3)
+    c_kv.fill_(cfg.S - cfg.L)
+    torch.cuda._sleep(int(cycles_per_ms * (2 * enqueue_s * 1e3 + 1.0)))
+    commit_pass()
+    torch.cuda.synchronize()
+    commit_us = float(np.mean([e[0].elapsed_time(e[1]) for e in c_evs]) * 1e3)
+    commit_bytes = 2 * (2 * B * cfg.Hkv * cfg.L * cfg.D + B * cfg.hidden) * esz   # read + write
+
     plen = pk["length"].cpu().numpy()
     work = step_bytes_and_flops(cfg, plen, kv_len_np, full)
     cand = B * cfg.W * cfg.L
@@ -265,6 +305,8 @@ def main():
         "attention_hbm": {"kernel": "rd_tree_attention", **roof("attention", "hbm")},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "gpu_ms_per_step": round(ms_gpu, 4),
+        "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
+                       "bytes_moved": int(commit_bytes)},
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or (B if cfg.candidates <= 400 else 2)

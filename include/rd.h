@@ -195,6 +195,42 @@ int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker,
                      int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
                      int32_t *accepted_tokens, rd_stream_t stream);
 
+/*
+ * After step 4 -- commit the accepted path.  [TRT] intro: the best path is
+ * accepted before the next drafting round, so its tokens join the context;
+ * [NEWS] "RNN draft model": the drafter continues from the target's latest
+ * token and the target's last hidden state.
+ * For request b with w = best_beam[b], n = accept_len[b], c = kv_len[b]
+ * (as rd_unpack_accept leaves them): candidates (b,w,0..n) -- the initial
+ * token and the n accepted drafts -- were verified over exactly their plain
+ * decoding context, so for j = 0..n and every KV head g
+ *   k_cache[b,g,c+j,:] = k_new[b, unpacker[b,w,j], g, :]   (v likewise),
+ * then kv_len[b] = c + n + 1, and, when hidden and hidden_next are given,
+ *   hidden_next[b,:] = hidden[b, unpacker[b,w,n], :]
+ * (the row whose logits chose the bonus token).  The bonus token itself has
+ * no key or value yet: it opens the next step's beams.
+ * A request with w outside [0,W), n outside [0,L-1], c < 0 or c+n+1 > S_max
+ * is left unchanged (cache rows, kv_len and its hidden_next row), so a
+ * caller sees an overflow as kv_len not moving.  Unpacker entries are
+ * clamped to [0, W*L).
+ *
+ *   unpacker (dev) [B,W,L]; best_beam, accept_len (dev) [B]
+ *   k_new, v_new (dev) [B,W*L,Hkv,D] in dtype (packed layout, read only)
+ *   hidden (dev) [B,W*L,K] or NULL; hidden_next (dev) [B,K] or NULL (both or neither)
+ *   k_cache, v_cache (dev) [B,Hkv,S_max,D] in dtype, updated in place
+ *   kv_len (dev) [B], read and advanced in place
+ * One launch.  The written cache rows must not overlap k_new, v_new or
+ * hidden.  Errors: RD_E_ARG for null required pointers, negative sizes,
+ * Hkv < 1, D < 1, or only one of hidden / hidden_next given;
+ * RD_E_UNSUPPORTED for W > 64, L > 16, an unknown dtype, or one request's
+ * rows exceeding 2^31 bytes.
+ */
+int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_beam,
+                       const int32_t *accept_len, const void *k_new, const void *v_new,
+                       const void *hidden, int B, int W, int L, int Hkv, int D, int K,
+                       int S_max, void *k_cache, void *v_cache, int32_t *kv_len,
+                       void *hidden_next, rd_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("rd_pack_beams", "rd_tree_mask", "rd_tree_attention", "rd_lm_head_argmax", "rd_unpack_accept"):
+    for n in ("rd_pack_beams", "rd_tree_mask", "rd_tree_attention", "rd_lm_head_argmax", "rd_unpack_accept",
+              "rd_commit_accepted"):
         assert n in names
     assert set(names) == set(rd.EXPORTED_SYMBOLS)
 
@@ -72,6 +73,16 @@ def test_host_side_validation_without_device():
     assert lib.rd_lm_head_argmax(1, fake, fake, fake, 0, 8, 128, 50, fake, fake, fake, 0, null) == 0
     # unpack/accept: unknown dtype
     assert lib.rd_unpack_accept(fake, fake, fake, fake, fake, 9, 8, 2, 4, 3, fake, fake, fake, fake, null) == -2
+    # commit: empty batch, null cache, hidden without hidden_next, zero heads, unknown dtype, L > 16
+    c = [fake] * 6      # unpacker, best_beam, accept_len, k_new, v_new, hidden
+    o = [fake] * 4      # k_cache, v_cache, kv_len, hidden_next
+    assert lib.rd_commit_accepted(1, *c, 0, 8, 5, 32, 128, 4096, 1024, *o, null) == 0
+    assert lib.rd_commit_accepted(1, *c, 2, 8, 5, 32, 128, 4096, 1024, null, fake, fake, fake, null) == -1
+    assert lib.rd_commit_accepted(1, *c, 2, 8, 5, 32, 128, 4096, 1024, fake, fake, fake, null, null) == -1
+    assert lib.rd_commit_accepted(1, *c, 2, 8, 5, 0, 128, 4096, 1024, *o, null) == -1
+    assert lib.rd_commit_accepted(1, *c, 2, 8, 5, 32, 128, 4096, -1, *o, null) == -1
+    assert lib.rd_commit_accepted(3, *c, 2, 8, 5, 32, 128, 4096, 1024, *o, null) == -2
+    assert lib.rd_commit_accepted(1, *c, 2, 8, 17, 32, 128, 4096, 1024, *o, null) == -2
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

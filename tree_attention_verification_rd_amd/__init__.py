@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
     "rd_pack_beams", "rd_tree_mask", "rd_tree_attention", "rd_tree_attention_workspace_size",
-    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "verify_step",
+    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "verify_step",
     "VerifyBuffers",
 ]
 
@@ -28,7 +28,7 @@ MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 EXPORTED_SYMBOLS = (
     "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_lm_head_workspace_size",
-    "rd_lm_head_argmax", "rd_unpack_accept",
+    "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,8 @@ def load_library():
         "rd_lm_head_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "rd_lm_head_argmax": ([i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
+        "rd_commit_accepted": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -247,6 +249,46 @@ def rd_unpack_accept(beams, unpacker, packed_argmax, packed=None, *, unpacked=No
                                 B, W, L, _p(res["match_len"]), _p(res["best_beam"]), _p(res["accept_len"]),
                                 _p(res["accepted_tokens"]), _stream(beams)), "rd_unpack_accept")
     return res
+
+
+def rd_commit_accepted(unpacker, best_beam, accept_len, k_new, v_new, k_cache, v_cache, kv_len, hidden=None, *,
+                       hidden_next=None):
+    """After step 4: append the accepted path's keys/values to the cache and advance kv_len, in place.
+
+    k_new/v_new are packed [B, W*L, Hkv, D]; k_cache/v_cache [B, Hkv, S, D]; hidden (optional) [B, W*L, K].
+    Returns hidden_next [B, K] (the drafter's hidden state) or None when hidden is None.  Requests
+    that would overflow the cache are left unchanged (their kv_len does not move).
+    """
+    lib = load_library()
+    _need(unpacker, "unpacker", torch.int32)
+    B, W, L = unpacker.shape
+    dev = unpacker.device
+    dt = _dtype_code(k_new)
+    _need(k_new, "k_new", k_new.dtype, None, dev)
+    if k_new.dim() != 4 or k_new.shape[0] != B or k_new.shape[1] != W * L:
+        raise ValueError("k_new must be [B, W*L, Hkv, D]")
+    Hkv, D = k_new.shape[2], k_new.shape[3]
+    _need(v_new, "v_new", k_new.dtype, (B, W * L, Hkv, D), dev)
+    _need(k_cache, "k_cache", k_new.dtype, None, dev)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[:2]) != (B, Hkv) or k_cache.shape[3] != D:
+        raise ValueError("k_cache must be [B, Hkv, S, D]")
+    S = k_cache.shape[2]
+    _need(v_cache, "v_cache", k_new.dtype, (B, Hkv, S, D), dev)
+    for t, name in ((best_beam, "best_beam"), (accept_len, "accept_len"), (kv_len, "kv_len")):
+        _need(t, name, torch.int32, (B,), dev)
+    K = 0
+    if hidden is not None:
+        _need(hidden, "hidden", k_new.dtype, None, dev)
+        if hidden.dim() != 3 or tuple(hidden.shape[:2]) != (B, W * L):
+            raise ValueError("hidden must be [B, W*L, K]")
+        K = hidden.shape[2]
+        hidden_next = _out(hidden_next, "hidden_next", (B, K), k_new.dtype, dev)
+    else:
+        hidden_next = None
+    _check(lib.rd_commit_accepted(dt, _p(unpacker), _p(best_beam), _p(accept_len), _p(k_new), _p(v_new), _p(hidden),
+                                  B, W, L, Hkv, D, K, S, _p(k_cache), _p(v_cache), _p(kv_len), _p(hidden_next),
+                                  _stream(unpacker)), "rd_commit_accepted")
+    return hidden_next
 
 
 class VerifyBuffers:

@@ -159,4 +159,24 @@ int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_
                                                accept_len, accepted_tokens, s));
 }
 
+int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,
+                       const void *k_new, const void *v_new, const void *hidden, int B, int W, int L, int Hkv,
+                       int D, int K, int S_max, void *k_cache, void *v_cache, int32_t *kv_len, void *hidden_next,
+                       rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L) || Hkv < 1 || D < 1 || K < 0 || S_max < 0) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!unpacker || !best_beam || !accept_len || !k_new || !v_new || !k_cache || !v_cache || !kv_len)
+        return RD_E_ARG;
+    if ((hidden != nullptr) != (hidden_next != nullptr) || (hidden && K < 1)) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    const int64_t esize = dtype == RD_F32 ? 4 : 2;
+    // copy units (2 bytes at the narrowest) of one request must index in 32 bits
+    const int64_t units = (2 * static_cast<int64_t>(Hkv) * L * D + (hidden ? K : 0)) * esize / 2;
+    if (units >= (1LL << 30)) return RD_E_UNSUPPORTED;
+    return hip_status(rd::launch_commit(static_cast<int>(esize), unpacker, best_beam, accept_len, k_new, v_new,
+                                        hidden, B, W, L, Hkv, D, K, S_max, k_cache, v_cache, kv_len, hidden_next,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"
