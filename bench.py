@@ -166,10 +166,8 @@ def main():
     def step(s, ev=None):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
-        rd.rd_pack_beams(beams, packed_tokens=pk["tokens"], packed_len=pk["length"], unpacker=pk["unpacker"],
-                         packed_depth=pk["depth"], packed_src=pk["src"])
-        rec(1)
-        rd.rd_tree_mask(pk["unpacker"], pk["length"], mask=bufs.mask)
+        rd.rd_pack_beams_mask(beams, packed_tokens=pk["tokens"], packed_len=pk["length"], unpacker=pk["unpacker"],
+                              packed_depth=pk["depth"], packed_src=pk["src"], mask=bufs.mask)
         rec(2)
         rd.rd_tree_attention(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], kv_len, bufs.mask,
                              pk["length"], out=bufs.attn, workspace=bufs.attn_ws)
@@ -221,8 +219,8 @@ def main():
     for i in range(K):
         step(sets[i % n_sets], evs[i])
     torch.cuda.synchronize()
-    names = ["pack", "mask", "attention", "lm_head", "unpack_accept"]
-    per_call_us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]) * 1e3) for j, n in enumerate(names)}
+    marks = {"pack_mask": (0, 2), "attention": (2, 3), "lm_head": (3, 4), "unpack_accept": (4, 5)}
+    per_call_us = {n: float(np.mean([e[j0].elapsed_time(e[j1]) for e in evs]) * 1e3) for n, (j0, j1) in marks.items()}
 
     # The commit of the accepted path, the call after the step (not part of
     # the timed step): timed alone, at full acceptance (n = L-1 on beam 0) so

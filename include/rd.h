@@ -115,6 +115,17 @@ int rd_pack_beams(const int32_t *beams, int B, int W, int L,
 int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int W, int L,
                  uint32_t *mask, rd_stream_t stream);
 
+/*
+ * Steps 1 and 1b in one launch: exactly rd_pack_beams followed by
+ * rd_tree_mask on its outputs (same arguments, same results), for callers
+ * that want both; the mask is built from the unpacker while it is still in
+ * on-chip memory.
+ */
+int rd_pack_beams_mask(const int32_t *beams, int B, int W, int L,
+                       int32_t *packed_tokens, int32_t *packed_len, int32_t *unpacker,
+                       int32_t *packed_depth, int32_t *packed_src, uint32_t *mask,
+                       rd_stream_t stream);
+
 /* Bytes of device workspace rd_tree_attention needs for these sizes (may be 0). */
 size_t rd_tree_attention_workspace_size(int dtype, int B, int P_max, int Hq, int Hkv, int D,
                                         int S_max);

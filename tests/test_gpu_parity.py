@@ -37,14 +37,17 @@ def dev_int(a):
 
 
 def check_pack(beams: np.ndarray):
+    """Separate pack and mask calls, and the fused call, against the oracle."""
     ref = oracle.pack_beams(beams)
     got = rd.rd_pack_beams(dev_int(beams))
     mask = rd.rd_tree_mask(got["unpacker"], got["length"])
+    fused, fmask = rd.rd_pack_beams_mask(dev_int(beams))
     torch.cuda.synchronize()
-    for key in ("tokens", "length", "unpacker", "depth", "src"):
-        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
     ref_bits = oracle.mask_to_bits(oracle.tree_mask(ref["unpacker"], ref["length"]))
-    np.testing.assert_array_equal(mask_words_np(mask), ref_bits, err_msg="mask")
+    for tag, g, m in (("separate", got, mask), ("fused", fused, fmask)):
+        for key in ("tokens", "length", "unpacker", "depth", "src"):
+            np.testing.assert_array_equal(g[key].cpu().numpy(), ref[key], err_msg=f"{tag} {key}")
+        np.testing.assert_array_equal(mask_words_np(m), ref_bits, err_msg=f"{tag} mask")
     return ref
 
 
@@ -87,6 +90,8 @@ def test_empty_inputs_are_noops():
     assert out["tokens"].shape == (0, 12)
     m = rd.rd_tree_mask(out["unpacker"], out["length"])
     assert m.shape == (0, 12, 1)
+    fo, fm = rd.rd_pack_beams_mask(e)
+    assert fo["tokens"].shape == (0, 12) and fm.shape == (0, 12, 1)
     for shape in ((3, 0, 4), (3, 4, 0)):
         t = torch.empty(shape, dtype=torch.int32, device="cuda")
         rd.rd_pack_beams(t)

@@ -60,6 +60,9 @@ def test_host_side_validation_without_device():
     fake = ctypes.c_void_p(0x1000)
     assert lib.rd_pack_beams(fake, 2, 65, 4, fake, fake, fake, null, null, null) == -2
     assert lib.rd_pack_beams(fake, 2, 4, 17, fake, fake, fake, null, null, null) == -2
+    assert lib.rd_pack_beams_mask(fake, 2, 4, 17, fake, fake, fake, null, null, fake, null) == -2
+    assert lib.rd_pack_beams_mask(fake, 2, 4, 4, fake, fake, fake, null, null, null, null) == -1
+    assert lib.rd_pack_beams_mask(null, 0, 4, 4, null, null, null, null, null, null, null) == 0
     # attention: unsupported dtype / head dim, bad head grouping, negative scale
     args = [fake] * 8
     assert lib.rd_tree_attention(7, *args, 2, 8, 4, 4, 128, 64, 0.0, fake, fake, 0, null) == -2

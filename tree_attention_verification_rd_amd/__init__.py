@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
-    "rd_pack_beams", "rd_tree_mask", "rd_tree_attention", "rd_tree_attention_workspace_size",
+    "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_tree_attention", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "verify_step",
     "VerifyBuffers",
 ]
@@ -26,7 +26,7 @@ RD_F32, RD_BF16 = 0, 1
 MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 
 EXPORTED_SYMBOLS = (
-    "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask",
+    "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted",
 )
@@ -61,6 +61,7 @@ def load_library():
         "rd_version": ([], i32),
         "rd_pack_beams": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "rd_tree_mask": ([vp, vp, i32, i32, i32, vp, vp], i32),
+        "rd_pack_beams_mask": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
         "rd_tree_attention_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "rd_tree_attention": ([i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                vp, vp, sz, vp], i32),
@@ -155,6 +156,29 @@ def rd_tree_mask(unpacker: torch.Tensor, packed_len: torch.Tensor, *, mask=None)
     mask = _out(mask, "mask", (B, P, (P + 31) // 32), torch.int32, unpacker.device)
     _check(lib.rd_tree_mask(_p(unpacker), _p(packed_len), B, W, L, _p(mask), _stream(unpacker)), "rd_tree_mask")
     return mask
+
+
+def rd_pack_beams_mask(beams: torch.Tensor, *, packed_tokens=None, packed_len=None, unpacker=None,
+                       packed_depth=None, packed_src=None, mask=None, with_depth_src: bool = True):
+    """Steps 1 + 1b in one launch: returns (pack dict as rd_pack_beams, mask as rd_tree_mask)."""
+    lib = load_library()
+    _need(beams, "beams", torch.int32)
+    if beams.dim() != 3:
+        raise ValueError("beams must be [B, W, L]")
+    B, W, L = beams.shape
+    dev = beams.device
+    P = W * L
+    out = {
+        "tokens": _out(packed_tokens, "packed_tokens", (B, P), torch.int32, dev),
+        "length": _out(packed_len, "packed_len", (B,), torch.int32, dev),
+        "unpacker": _out(unpacker, "unpacker", (B, W, L), torch.int32, dev),
+        "depth": _out(packed_depth, "packed_depth", (B, P), torch.int32, dev) if with_depth_src else None,
+        "src": _out(packed_src, "packed_src", (B, P), torch.int32, dev) if with_depth_src else None,
+    }
+    mask = _out(mask, "mask", (B, P, (P + 31) // 32), torch.int32, dev)
+    _check(lib.rd_pack_beams_mask(_p(beams), B, W, L, _p(out["tokens"]), _p(out["length"]), _p(out["unpacker"]),
+                                  _p(out["depth"]), _p(out["src"]), _p(mask), _stream(beams)), "rd_pack_beams_mask")
+    return out, mask
 
 
 def rd_tree_attention_workspace_size(dtype_code: int, B, P_max, Hq, Hkv, D, S_max) -> int:
@@ -314,16 +338,15 @@ class VerifyBuffers:
 
 def verify_step(beams, q, k_new, v_new, k_cache, v_cache, kv_len, hidden, weight, *, want_logits=True,
                 buffers: VerifyBuffers | None = None, scale: float = 0.0) -> dict:
-    """One verification step: the five entry points enqueued in order on the current stream.
+    """One verification step: pack+mask, attention, projection, unpack+accept, enqueued in order on the current stream.
 
     q/k_new/v_new/hidden are in packed layout [B, W*L, ...] (rows past the packed length are ignored).
     """
     B, W, L = beams.shape
     bufs = buffers
-    pk = rd_pack_beams(beams, **({} if bufs is None else {
+    pk, mask = rd_pack_beams_mask(beams, **({} if bufs is None else {
         "packed_tokens": bufs.pack["tokens"], "packed_len": bufs.pack["length"], "unpacker": bufs.pack["unpacker"],
-        "packed_depth": bufs.pack["depth"], "packed_src": bufs.pack["src"]}))
-    mask = rd_tree_mask(pk["unpacker"], pk["length"], mask=None if bufs is None else bufs.mask)
+        "packed_depth": bufs.pack["depth"], "packed_src": bufs.pack["src"], "mask": bufs.mask}))
     attn = rd_tree_attention(q, k_new, v_new, k_cache, v_cache, kv_len, mask, pk["length"], scale=scale,
                              out=None if bufs is None else bufs.attn,
                              workspace=None if bufs is None else bufs.attn_ws)

@@ -61,6 +61,17 @@ int rd_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *packed_tok
                                             packed_src, as_stream(stream)));
 }
 
+int rd_pack_beams_mask(const int32_t *beams, int B, int W, int L, int32_t *packed_tokens, int32_t *packed_len,
+                       int32_t *unpacker, int32_t *packed_depth, int32_t *packed_src, uint32_t *mask,
+                       rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L)) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!beams || !packed_tokens || !packed_len || !unpacker || !mask) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    return hip_status(rd::launch_pack_mask(beams, B, W, L, packed_tokens, packed_len, unpacker, packed_depth,
+                                           packed_src, mask, as_stream(stream)));
+}
+
 int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int W, int L, uint32_t *mask,
                  rd_stream_t stream) {
     if (!beam_shape_ok(B, W, L)) return RD_E_ARG;

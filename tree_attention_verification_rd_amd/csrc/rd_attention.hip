@@ -76,7 +76,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4 *>(static_cast<uintptr_t>(addr)));
 }
 
-template <int D, int QPW, int NWAVE, int KSPLIT, int NS>
+// Rows of query block qi of query group q: blocked, rows row0 + (NQG*qi +
+// q)*16 + (0..15), or, with LI (lane-interleaved, for few rows), rows
+// row0 + (16*qi + j)*NQG + q for lane j, so a handful of rows still gives
+// every query group -- and so every wavefront -- work.
+template <int D, int QPW, int NWAVE, int KSPLIT, int NS, bool LI>
 __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     constexpr int NKC = D / 32;              // k-steps over the head dim (QK^T)
     constexpr int NDB = D / 16;              // 16-row blocks of the head dim (PV)
@@ -115,6 +119,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     const int lane = tid & 63;
     const int lq = lane & 15;
     const int kg = lane >> 4;
+    auto row_of = [&](int qi, int j) {  // row of lane slot j in this group's block qi, relative to row0
+        return LI ? (16 * qi + j) * NQG + wq : (NQG * qi + wq) * 16 + j;
+    };
 
     const int Pb = min(max(a.plen[b], 0), a.P);
     const int kvl = min(max(a.kv_len[b], 0), a.S_max);
@@ -370,15 +377,13 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     // every wait counts the same number of loads.
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue_tile(st, st);
-    // this lane's query rows: block qi of query group q covers rows
-    // row0 + (NQG*qi + q)*16 .. +15 (interleaved, so few rows still spread
-    // over the groups).  Valid blocks form a prefix in qi; a wavefront
-    // multiplies only its valid ones (none: it only helps with the loads).
+    // this lane's query rows (row_of).  Valid blocks form a prefix in qi; a
+    // wavefront multiplies only its valid ones (none: it only helps with the
+    // loads).
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
-        const int rbase = row0 + (NQG * qi + wq) * 16;
-        nact += (rbase < Mb) ? 1 : 0;
-        const int r = rbase + lq;
+        nact += (row0 + row_of(qi, 0) < Mb) ? 1 : 0;
+        const int r = row0 + row_of(qi, lq);
         const bool rvalid = r < Mb;
         const int p = rvalid ? r / a.G : 0;
         const int h = g * a.G + (rvalid ? r % a.G : 0);
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
 
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
-        const int r = row0 + (NQG * qi + wq) * 16 + lq;
+        const int r = row0 + row_of(qi, lq);
         const bool rvalid = r < Mb;
         if (a.nsplit == 1) {
             // o[qi][db][e] = O[query r][d = db*16 + 4*kg + e]; padding rows get zeros
@@ -642,6 +647,11 @@ AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int
     plan.qpw = 2;
     plan.nwave = rows <= 128 ? 4 : 8;
     plan.ksplit = rows <= 64 ? 2 : 1;
+    if (rows <= 64 && env_int("RD_ATTN_FEWROW", 1) == 1) {
+        // (1, 8, 2) with lane-interleaved rows: four query groups of ~rows/4
+        plan.qpw = 1;
+        plan.nwave = 8;
+    }
     const int rb = 16 * plan.qpw * plan.nwave / plan.ksplit;
     plan.nqblk = (rows + rb - 1) / rb;
     plan.rows_unit = plan.nqblk * rb;
@@ -710,15 +720,21 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
     const dim3 blk(64 * plan.nwave);
     // ring depth: three stages (measured on MI355X: two starve the MFMA-heavy
     // shapes, four did not stream faster)
-    if (D == 64) {
-        if (plan.ksplit == 2) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4, 2, 3>), grid, blk, 0, stream, a);
-        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 4, 1, 3>), grid, blk, 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_attn_bf16<64, 2, 8, 1, 3>), grid, blk, 0, stream, a);
-    } else {
-        if (plan.ksplit == 2) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4, 2, 3>), grid, blk, 0, stream, a);
-        else if (plan.nwave == 4) hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 4, 1, 3>), grid, blk, 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_attn_bf16<128, 2, 8, 1, 3>), grid, blk, 0, stream, a);
-    }
+    auto go = [&](auto d_c) {
+        constexpr int DD = decltype(d_c)::value;
+        if (plan.ksplit == 2 && plan.qpw == 1)
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 1, 8, 2, 3, true>), grid, blk, 0, stream, a);
+        else if (plan.ksplit == 2)
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 2, 3, false>), grid, blk, 0, stream, a);
+        else if (plan.nwave == 4)
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 1, 3, false>), grid, blk, 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 8, 1, 3, false>), grid, blk, 0, stream, a);
+    };
+    if (D == 64)
+        go(std::integral_constant<int, 64>{});
+    else
+        go(std::integral_constant<int, 128>{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || plan.nsplit == 1) return err;
     const unsigned ncomb = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * (plan.rows_unit / kCombRows));

@@ -13,6 +13,8 @@ constexpr int kMaxBeamLen = 16;
 hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *tokens,
                              int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
                              hipStream_t stream);
+hipError_t launch_pack_mask(const int32_t *beams, int B, int W, int L, int32_t *tokens, int32_t *plen,
+                            int32_t *unpacker, int32_t *depth, int32_t *src, uint32_t *mask, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t *unpacker, const int32_t *plen, int B, int W, int L,
                             uint32_t *mask, hipStream_t stream);
 

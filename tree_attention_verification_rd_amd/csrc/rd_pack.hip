@@ -17,24 +17,25 @@
 
 namespace rd {
 
-__global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ beams, int W, int L,
-                                                   int32_t *__restrict__ tokens,
-                                                   int32_t *__restrict__ plen,
-                                                   int32_t *__restrict__ unpacker,
-                                                   int32_t *__restrict__ depth,
-                                                   int32_t *__restrict__ src) {
-    __shared__ int32_t sb[kMaxBeams * kMaxBeamLen];
-    const int b = blockIdx.x;
+// Packs request b with one wavefront (lane = beam) and no workgroup
+// barrier, so it can run in the first wavefront of a larger workgroup.
+// When su (LDS) is given the unpacker row of every beam is also left there
+// for the fused mask.  Returns the packed length (in every lane).
+__device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, int b, int W, int L,
+                                            int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
+                                            int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
+                                            int32_t *__restrict__ src, int32_t *su) {
     const int lane = threadIdx.x;
     const int P = W * L;
     const int32_t *bb = beams + static_cast<size_t>(b) * P;
-    for (int i = lane; i < P; i += kWave) sb[i] = bb[i];
-    __syncthreads();
 
     const bool active = lane < W;
-    int own[kMaxBeamLen];
+    int own[kMaxBeamLen];  // index clamped inside the request: the loads issue together, unguarded
 #pragma unroll
-    for (int l = 0; l < kMaxBeamLen; ++l) own[l] = (active && l < L) ? sb[lane * L + l] : 0;
+    for (int l = 0; l < kMaxBeamLen; ++l) {
+        const int t = bb[min(lane * L + l, P - 1)];
+        own[l] = (active && l < L) ? t : 0;
+    }
 
     int m = 0;                  // longest prefix shared with an earlier beam
     int first[kMaxBeamLen];     // lowest beam sharing the prefix of length l+1
@@ -42,12 +43,13 @@ __global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ b
     for (int l = 0; l < kMaxBeamLen; ++l) first[l] = lane;
 
     for (int v = 0; v < W; ++v) {  // uniform across the wave
+        // beam v's tokens are lane v's own[]: read across lanes, no LDS trips
         int lcp = 0;
         bool run = true;
 #pragma unroll
         for (int l = 0; l < kMaxBeamLen; ++l) {
             if (l < L) {
-                run = run && (sb[v * L + l] == own[l]);
+                run = run && (__builtin_amdgcn_readlane(own[l], v) == own[l]);
                 lcp += run ? 1 : 0;
             }
         }
@@ -77,7 +79,10 @@ __global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ b
             const int owner = first[l];
             const int owner_base = __shfl(base, owner, kWave);
             const int owner_m = __shfl(m, owner, kWave);
-            if (active) urow[l] = owner_base + l - owner_m;
+            if (active) {
+                urow[l] = owner_base + l - owner_m;
+                if (su) su[lane * L + l] = owner_base + l - owner_m;
+            }
         }
     }
 
@@ -99,21 +104,29 @@ __global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ b
         if (src) src[row + s] = -1;
     }
     if (lane == 0) plen[b] = total;
+    return total;
+}
+
+__global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ beams, int W, int L,
+                                                   int32_t *__restrict__ tokens,
+                                                   int32_t *__restrict__ plen,
+                                                   int32_t *__restrict__ unpacker,
+                                                   int32_t *__restrict__ depth,
+                                                   int32_t *__restrict__ src) {
+    pack_request(beams, blockIdx.x, W, L, tokens, plen, unpacker, depth, src, nullptr);
 }
 
 // Step 1b.  [SURV] SpecInfer "Token Tree Verifier": bit q of row p is set iff
 // slot q is p or an ancestor of p.  The parent of slot unpacker[w,l] is
 // unpacker[w,l-1]; every candidate that maps to a slot names the same
 // parent, so concurrent writers store the same value.  Each thread then
-// builds one mask word by walking at most L parent links.
-__global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ unpacker,
-                                                   const int32_t *__restrict__ plen, int W, int L,
-                                                   uint32_t *__restrict__ mask) {
-    __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
-    const int b = blockIdx.x;
+// builds one mask word by walking at most L parent links.  u is request b's
+// unpacker row block (global or LDS), n its packed length; parent is LDS
+// scratch of kMaxBeams*kMaxBeamLen ints.
+__device__ __forceinline__ void mask_request(const int32_t *u, int n, int b, int W, int L, int32_t *parent,
+                                             uint32_t *__restrict__ mask) {
     const int P = W * L;
     const int nw = (P + 31) / 32;
-    const int32_t *u = unpacker + static_cast<size_t>(b) * P;
     for (int i = threadIdx.x; i < P; i += blockDim.x) parent[i] = -1;
     __syncthreads();
     for (int i = threadIdx.x; i < P; i += blockDim.x) {
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ u
         if (p >= 0 && p < P) parent[p] = (l == 0) ? -1 : u[i - 1];
     }
     __syncthreads();
-    const int n = min(max(plen[b], 0), P);
+    n = min(max(n, 0), P);
     uint32_t *out = mask + static_cast<size_t>(b) * P * nw;
     for (int i = threadIdx.x; i < P * nw; i += blockDim.x) {
         const int p = i / nw;
@@ -139,11 +152,44 @@ __global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ u
     }
 }
 
+__global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ unpacker,
+                                                   const int32_t *__restrict__ plen, int W, int L,
+                                                   uint32_t *__restrict__ mask) {
+    __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
+    const int b = blockIdx.x;
+    mask_request(unpacker + static_cast<size_t>(b) * W * L, plen[b], b, W, L, parent, mask);
+}
+
+// Steps 1 and 1b in one launch: the first wavefront packs the request and
+// leaves its unpacker in LDS, then the workgroup builds the mask from it.
+__global__ __launch_bounds__(256) void k_pack_mask(const int32_t *__restrict__ beams, int W, int L,
+                                                   int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
+                                                   int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
+                                                   int32_t *__restrict__ src, uint32_t *__restrict__ mask) {
+    __shared__ int32_t su[kMaxBeams * kMaxBeamLen];
+    __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
+    __shared__ int32_t n_sh;
+    const int b = blockIdx.x;
+    if (threadIdx.x < kWave) {  // wave-uniform branch; the pack has no workgroup barrier
+        const int n = pack_request(beams, b, W, L, tokens, plen, unpacker, depth, src, su);
+        if (threadIdx.x == 0) n_sh = n;
+    }
+    __syncthreads();
+    mask_request(su, n_sh, b, W, L, parent, mask);
+}
+
 hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *tokens,
                              int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
                              hipStream_t stream) {
     hipLaunchKernelGGL(k_pack_beams, dim3(B), dim3(kWave), 0, stream, beams, W, L, tokens, plen,
                        unpacker, depth, src);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_mask(const int32_t *beams, int B, int W, int L, int32_t *tokens, int32_t *plen,
+                            int32_t *unpacker, int32_t *depth, int32_t *src, uint32_t *mask, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pack_mask, dim3(B), dim3(256), 0, stream, beams, W, L, tokens, plen, unpacker, depth, src,
+                       mask);
     return hipGetLastError();
 }
 
