@@ -4,61 +4,55 @@
 // "Dynamic tree attention"; ReDrafter paper abstract, point 2): a slot per
 // distinct prefix.  Slot order is the first occurrence in a beam-major scan.
 //
-// One wavefront per request, one lane per beam.  Lane w finds, by comparing
-// its beam against every earlier beam, m_w = the longest prefix it shares
-// with any earlier beam, and for each depth l the lowest beam whose prefix
-// of length l+1 equals its own.  Beam w contributes the L - m_w new slots
-// at depths m_w..L-1; their positions come from an exclusive prefix sum of
-// those counts across lanes, built from five ballots (one per bit of the
-// count) and popcounts of the lanes below.  Depths l < m_w reuse the slot
-// that the first sharing beam owns, read from that lane by a shuffle.
+// One wavefront per request, one lane per beam.  Depth by depth, the node
+// of (beam w, depth l) is the pair (node at depth l-1, token at l); lane w
+// names it by f_l(w), the lowest beam with the same pair (w itself when no
+// earlier beam shares the prefix), found by reading every other lane's
+// parent name and token with v_readlane -- W*L iterations of a few
+// branch-free instructions.  A prefix shared with an earlier beam stays
+// shared at every shallower depth, so m_w = #{l : f_l(w) < w} is the length
+// of the prefix beam w shares with an earlier beam.  Beam w contributes the L - m_w new slots at depths
+// m_w..L-1; their positions come from an exclusive prefix sum of those
+// counts across lanes, built from five ballots (one per bit of the count)
+// and popcounts of the lanes below.  Slot of (w, l) = base(o) + l - m(o)
+// with o = f_l(w), read from lane o by a shuffle.
 #include "rd_common.h"
 #include "rd_internal.h"
 
 namespace rd {
 
-// Packs request b with one wavefront (lane = beam) and no workgroup
-// barrier, so it can run in the first wavefront of a larger workgroup.
-// When su (LDS) is given the unpacker row of every beam is also left there
-// for the fused mask.  Returns the packed length (in every lane).
+// Packs request b with one wavefront and no workgroup barrier, so it can
+// run in the first wavefront of a larger workgroup.  sb and sf are LDS
+// scratch of W*L ints (the beams, the node names); when su (LDS) is given
+// the unpacker rows are also left there for the fused mask.  Returns the
+// packed length (in every lane).
 __device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, int b, int W, int L,
                                             int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
                                             int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
-                                            int32_t *__restrict__ src, int32_t *su) {
-    const int lane = threadIdx.x;
+                                            int32_t *__restrict__ src, int32_t *sb, int32_t *sf, int32_t *su) {
+    const int lane = threadIdx.x & (kWave - 1);
     const int P = W * L;
     const int32_t *bb = beams + static_cast<size_t>(b) * P;
+    for (int i = lane; i < P; i += kWave) sb[i] = bb[i];
+    // only this wavefront touches sb/sf: LDS keeps one wavefront's accesses
+    // in order, so completing its own writes is enough
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     const bool active = lane < W;
-    int own[kMaxBeamLen];  // index clamped inside the request: the loads issue together, unguarded
-#pragma unroll
-    for (int l = 0; l < kMaxBeamLen; ++l) {
-        const int t = bb[min(lane * L + l, P - 1)];
-        own[l] = (active && l < L) ? t : 0;
-    }
-
-    int m = 0;                  // longest prefix shared with an earlier beam
-    int first[kMaxBeamLen];     // lowest beam sharing the prefix of length l+1
-#pragma unroll
-    for (int l = 0; l < kMaxBeamLen; ++l) first[l] = lane;
-
-    for (int v = 0; v < W; ++v) {  // uniform across the wave
-        // beam v's tokens are lane v's own[]: read across lanes, no LDS trips
-        int lcp = 0;
-        bool run = true;
-#pragma unroll
-        for (int l = 0; l < kMaxBeamLen; ++l) {
-            if (l < L) {
-                run = run && (__builtin_amdgcn_readlane(own[l], v) == own[l]);
-                lcp += run ? 1 : 0;
-            }
+    const int own0 = active ? lane * L : 0;
+    int fprev = 0;  // every beam hangs off the same virtual root
+    int m = 0;
+    for (int l = 0; l < L; ++l) {  // uniform
+        const int tok = sb[own0 + l];
+        int f = lane;
+        for (int v = 0; v < W; ++v) {  // uniform
+            const int pv = __builtin_amdgcn_readlane(fprev, v);
+            const int tv = __builtin_amdgcn_readlane(tok, v);
+            f = (v < f && pv == fprev && tv == tok) ? v : f;
         }
-        if (active && v < lane) {
-            m = max(m, lcp);
-#pragma unroll
-            for (int l = 0; l < kMaxBeamLen; ++l)
-                if (l < lcp && first[l] == lane) first[l] = v;
-        }
+        if (active) sf[own0 + l] = f;
+        m += (f < lane) ? 1 : 0;
+        fprev = f;
     }
 
     // exclusive prefix sum of new-slot counts over lanes, bit plane by bit plane
@@ -71,30 +65,20 @@ __device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, i
         base += __popcll(bal & below) << bit;
         total += __popcll(bal) << bit;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    int32_t *urow = unpacker + (static_cast<size_t>(b) * W + (active ? lane : 0)) * L;
-#pragma unroll
-    for (int l = 0; l < kMaxBeamLen; ++l) {
-        if (l < L) {  // uniform: every lane takes part in the shuffles
-            const int owner = first[l];
-            const int owner_base = __shfl(base, owner, kWave);
-            const int owner_m = __shfl(m, owner, kWave);
-            if (active) {
-                urow[l] = owner_base + l - owner_m;
-                if (su) su[lane * L + l] = owner_base + l - owner_m;
-            }
-        }
-    }
-
+    int32_t *urow = unpacker + static_cast<size_t>(b) * P + own0;
     const size_t row = static_cast<size_t>(b) * P;
-    if (active) {
-#pragma unroll
-        for (int l = 0; l < kMaxBeamLen; ++l) {
-            if (l < L && l >= m) {
-                const int slot = base + l - m;
-                tokens[row + slot] = own[l];
+    for (int l = 0; l < L; ++l) {  // uniform: every lane takes part in the shuffles
+        const int o = sf[own0 + l];
+        const int slot = __shfl(base, o, kWave) + l - __shfl(m, o, kWave);
+        if (active) {
+            urow[l] = slot;
+            if (su) su[own0 + l] = slot;
+            if (l >= m) {  // a node this beam opens
+                tokens[row + slot] = sb[own0 + l];
                 if (depth) depth[row + slot] = l;
-                if (src) src[row + slot] = lane * L + l;
+                if (src) src[row + slot] = own0 + l;
             }
         }
     }
@@ -113,7 +97,9 @@ __global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ b
                                                    int32_t *__restrict__ unpacker,
                                                    int32_t *__restrict__ depth,
                                                    int32_t *__restrict__ src) {
-    pack_request(beams, blockIdx.x, W, L, tokens, plen, unpacker, depth, src, nullptr);
+    __shared__ int32_t sb[kMaxBeams * kMaxBeamLen];
+    __shared__ int32_t sf[kMaxBeams * kMaxBeamLen];
+    pack_request(beams, blockIdx.x, W, L, tokens, plen, unpacker, depth, src, sb, sf, nullptr);
 }
 
 // Step 1b.  [SURV] SpecInfer "Token Tree Verifier": bit q of row p is set iff
@@ -166,12 +152,14 @@ __global__ __launch_bounds__(256) void k_pack_mask(const int32_t *__restrict__ b
                                                    int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
                                                    int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
                                                    int32_t *__restrict__ src, uint32_t *__restrict__ mask) {
+    __shared__ int32_t sb[kMaxBeams * kMaxBeamLen];
+    __shared__ int32_t sf[kMaxBeams * kMaxBeamLen];
     __shared__ int32_t su[kMaxBeams * kMaxBeamLen];
     __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
     __shared__ int32_t n_sh;
     const int b = blockIdx.x;
     if (threadIdx.x < kWave) {  // wave-uniform branch; the pack has no workgroup barrier
-        const int n = pack_request(beams, b, W, L, tokens, plen, unpacker, depth, src, su);
+        const int n = pack_request(beams, b, W, L, tokens, plen, unpacker, depth, src, sb, sf, su);
         if (threadIdx.x == 0) n_sh = n;
     }
     __syncthreads();
