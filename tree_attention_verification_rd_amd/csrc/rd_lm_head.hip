@@ -462,13 +462,25 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const float *__restrict__
     }
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int i = lane; i < nvt; i += kWave) {
-        const float v = pval[pr * nvt + i];
-        const int ix = pidx[pr * nvt + i];
-        if (better(v, ix, bv, bi)) {
-            bv = v;
-            bi = ix;
+    // four independent loads per lane per round (index clamped into the row,
+    // extras masked), so a row of up to 256 tiles costs one memory round trip
+    const float *rv = pval + pr * nvt;
+    const int32_t *ri = pidx + pr * nvt;
+    for (int i0 = 0; i0 < nvt; i0 += 4 * kWave) {
+        float v[4];
+        int ix[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = min(i0 + u * kWave + lane, nvt - 1);
+            v[u] = rv[i];
+            ix[u] = ri[i];
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * kWave + lane < nvt && better(v[u], ix[u], bv, bi)) {
+                bv = v[u];
+                bi = ix[u];
+            }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
