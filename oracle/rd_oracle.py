@@ -32,7 +32,9 @@ commit of the accepted path is pinned by decoding over the committed cache
 (torch scaled-dot-product attention must reproduce verification's output
 for every accepted candidate), by the committed rows spelling the text that
 the greedy accept reports, and by the chosen hidden state re-deriving the
-bonus token.
+bonus token.  Paged attention is pinned by pools cut from a contiguous cache
+with numpy reshapes (identity page tables reproduce contiguous attention
+exactly) and by invariance under permuting the pool's pages.
 """
 from __future__ import annotations
 
@@ -42,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "pack_beams", "tree_mask", "mask_to_bits", "attention_per_beam",
-    "attention_packed", "lm_head_logits", "argmax_first", "unpack",
+    "attention_packed", "gather_pages", "attention_paged", "lm_head_logits", "argmax_first", "unpack",
     "greedy_accept", "commit_accepted", "verify_requests",
 ]
 
@@ -204,6 +206,37 @@ def attention_packed(q, k, v, k_cache, v_cache, kv_len, mask, packed_len, scale=
             o = np.stack([_softmax_weighted_sum(scores[g], vals[g]) for g in range(Hkv)])
             out[b, p] = o.reshape(Hq, D)
     return out
+
+
+def gather_pages(pages: np.ndarray, block_table: np.ndarray, kv_len: np.ndarray) -> np.ndarray:
+    """Logical KV cache of each request from a paged pool.
+
+    [TRT] intro: the engine keeps its KV cache in pages (paged KV caching).
+    Reading (the pages name the feature, not a layout): pages is
+    [num_pages, Hkv, page_size, D]; key t of request b lives in page
+    block_table[b, t // page_size] at slot t % page_size.  Only keys
+    t < kv_len[b] are read (table entries past them may be anything).
+    Returns [B, Hkv, max(kv_len), D] with zeros past each kv_len.
+    """
+    ps = pages.shape[2]
+    B = block_table.shape[0]
+    S = int(max(int(x) for x in kv_len)) if B else 0
+    out = np.zeros((B, pages.shape[1], S, pages.shape[3]), pages.dtype)
+    for b in range(B):
+        for t in range(int(kv_len[b])):
+            out[b, :, t] = pages[int(block_table[b, t // ps]), :, t % ps]
+    return out
+
+
+def attention_paged(q, k, v, k_pages, v_pages, block_table, kv_len, mask, packed_len, scale=None) -> np.ndarray:
+    """Tree attention whose cached keys/values come from a paged pool.
+
+    The plain definition: gather each request's logical cache from the pool
+    (gather_pages), then attend exactly as attention_packed does.
+    """
+    kc = gather_pages(k_pages, block_table, kv_len)
+    vc = gather_pages(v_pages, block_table, kv_len)
+    return attention_packed(q, k, v, kc, vc, kv_len, mask, packed_len, scale)
 
 
 # ---------------------------------------------------------------- step 3 --
