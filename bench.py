@@ -222,44 +222,86 @@ def main():
     marks = {"pack_mask": (0, 2), "attention": (2, 3), "lm_head": (3, 4), "unpack_accept": (4, 5)}
     per_call_us = {n: float(np.mean([e[j0].elapsed_time(e[j1]) for e in evs]) * 1e3) for n, (j0, j1) in marks.items()}
 
+    def queued_call_us(call, prepare):
+        """Mean GPU time of call(i), i < K, run back to back.  A call can be
+        shorter than its host-side enqueue, so a busy-wait kernel sized to the
+        measured enqueue time goes first: the calls then queue up behind it
+        and the events time the GPU, not the host.  prepare() restores any
+        state the calls consume and runs before each pass, outside the events."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+
+        def run():
+            for i in range(K):
+                evs[i][0].record()
+                call(i)
+                evs[i][1].record()
+
+        prepare()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        run()
+        enqueue_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        cal = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        cal[0].record()
+        torch.cuda._sleep(1_000_000)
+        cal[1].record()
+        torch.cuda.synchronize()
+        cycles_per_ms = 1_000_000 / max(cal[0].elapsed_time(cal[1]), 1e-3)
+        prepare()
+        torch.cuda._sleep(int(cycles_per_ms * (2 * enqueue_s * 1e3 + 1.0)))
+        run()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+
     # The commit of the accepted path, the call after the step (not part of
-    # the timed step): timed alone, at full acceptance (n = L-1 on beam 0) so
-    # every request appends L rows per KV head.  Call i advances its own
-    # kv_len row, so no reset runs between calls.  The kernel is shorter than
-    # its host-side enqueue, so a busy-wait kernel sized to the measured
-    # enqueue time goes first: the calls then run back to back and the
-    # events time the GPU, not the host.
+    # the timed step): at full acceptance (n = L-1 on beam 0) every request
+    # appends L rows per KV head; call i advances its own kv_len row.
     c_best = torch.zeros(B, dtype=torch.int32, device=dev)
     c_nacc = torch.full((B,), cfg.L - 1, dtype=torch.int32, device=dev)
     c_kv = torch.empty((K, B), dtype=torch.int32, device=dev)
     c_hid = torch.empty((B, cfg.hidden), dtype=dt, device=dev)
-    c_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
 
-    def commit_pass():
-        for i in range(K):
-            s = sets[i % n_sets]
-            c_evs[i][0].record()
-            rd.rd_commit_accepted(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], s["k_cache"],
-                                  s["v_cache"], c_kv[i], s["hidden"], hidden_next=c_hid)
-            c_evs[i][1].record()
+    def commit_call(i):
+        s = sets[i % n_sets]
+        rd.rd_commit_accepted(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], s["k_cache"], s["v_cache"],
+                              c_kv[i], s["hidden"], hidden_next=c_hid)
 
-    c_kv.fill_(cfg.S - cfg.L)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    commit_pass()
-    enqueue_s = time.perf_counter() - h0
-    torch.cuda.synchronize()
-    cal = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    cal[0].record()
-    torch.cuda._sleep(1_000_000)
-    cal[1].record()
-    torch.cuda.synchronize()
-    cycles_per_ms = 1_000_000 / max(cal[0].elapsed_time(cal[1]), 1e-3)
-    c_kv.fill_(cfg.S - cfg.L)
-    torch.cuda._sleep(int(cycles_per_ms * (2 * enqueue_s * 1e3 + 1.0)))
-    commit_pass()
-    torch.cuda.synchronize()
-    commit_us = float(np.mean([e[0].elapsed_time(e[1]) for e in c_evs]) * 1e3)
+    commit_us = queued_call_us(commit_call, lambda: c_kv.fill_(cfg.S - cfg.L))
+
+    # Tree attention over a paged cache (the same keys, cut into 64-token
+    # pages of a pool in random order, one pool per input set).
+    ps = 64
+    npg = (cfg.S + ps - 1) // ps
+    pools = []
+    for si, s in enumerate(sets):
+        gperm = torch.Generator()
+        gperm.manual_seed(1000 + si)
+        perm = torch.randperm(B * npg, generator=gperm).to(dev)
+        pool = []
+        for c in (s["k_cache"], s["v_cache"]):
+            cp = torch.nn.functional.pad(c, (0, 0, 0, npg * ps - cfg.S)) if npg * ps != cfg.S else c
+            cut = cp.reshape(B, cfg.Hkv, npg, ps, cfg.D).permute(0, 2, 1, 3, 4).reshape(B * npg, cfg.Hkv, ps, cfg.D)
+            p_ = torch.empty_like(cut)
+            p_[perm] = cut
+            pool.append(p_)
+        pools.append((pool[0], pool[1], perm.reshape(B, npg).to(torch.int32).contiguous()))
+    paged_ws = torch.empty(max(rd.rd_tree_attention_workspace_size(1 if cfg.dtype == "bf16" else 0, B, P, cfg.Hq,
+                                                                  cfg.Hkv, cfg.D, npg * ps), 1),
+                           dtype=torch.uint8, device=dev)
+    paged_out = torch.empty_like(bufs.attn)
+
+    def paged_call(i):
+        s = sets[i % n_sets]
+        kp, vp, tbl = pools[i % n_sets]
+        rd.rd_tree_attention_paged(s["q"], s["k_new"], s["v_new"], kp, vp, tbl, kv_len, bufs.mask, pk["length"],
+                                   out=paged_out, workspace=paged_ws)
+
+    paged_us = queued_call_us(paged_call, lambda: None)
+    contig_us = queued_call_us(lambda i: rd.rd_tree_attention(
+        sets[i % n_sets]["q"], sets[i % n_sets]["k_new"], sets[i % n_sets]["v_new"], sets[i % n_sets]["k_cache"],
+        sets[i % n_sets]["v_cache"], kv_len, bufs.mask, pk["length"], out=paged_out, workspace=bufs.attn_ws),
+        lambda: None)
     commit_bytes = 2 * (2 * B * cfg.Hkv * cfg.L * cfg.D + B * cfg.hidden) * esz   # read + write
 
     plen = pk["length"].cpu().numpy()
@@ -305,6 +347,11 @@ def main():
         "gpu_ms_per_step": round(ms_gpu, 4),
         "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
                        "bytes_moved": int(commit_bytes)},
+        "attention_paged": {"call": "rd_tree_attention_paged", "page_size": ps, "avg_us": round(paged_us, 2),
+                            "contiguous_avg_us": round(contig_us, 2),
+                            "achieved": round(work["attention"][0] / (paged_us * 1e-6) / 1e9, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(work["attention"][0] / (paged_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or (B if cfg.candidates <= 400 else 2)

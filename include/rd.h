@@ -157,6 +157,30 @@ int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v
                       int B, int P_max, int Hq, int Hkv, int D, int S_max, float scale,
                       void *out, void *ws, size_t ws_bytes, rd_stream_t stream);
 
+/*
+ * Step 2 over a paged KV cache.  [TRT] intro: the engine keeps its KV cache
+ * in pages (paged KV caching).  Identical to rd_tree_attention except where
+ * cached keys come from: key t (< kv_len[b]) of request b is row
+ * t % page_size of page block_table[b, t / page_size] in the pools
+ *   k_pages, v_pages (dev) [num_pages, Hkv, page_size, D] in dtype.
+ *   block_table (dev) int32 [B, max_pages]; entries past a request's
+ *           kv_len are not read; page ids are clamped to [0, num_pages).
+ *   kv_len  (dev) [B], clamped to max_pages * page_size.
+ * Pages may be shared between requests (a common prefix).  Workspace:
+ * rd_tree_attention_workspace_size(dtype, B, P_max, Hq, Hkv, D,
+ * max_pages * page_size).  With the same keys and values the results equal
+ * rd_tree_attention's.
+ * Limits: as rd_tree_attention; for RD_BF16 page_size must be a multiple of
+ * 64 (RD_E_UNSUPPORTED otherwise); RD_E_ARG for page_size < 1, negative
+ * num_pages or max_pages, or null pools/table when max_pages > 0.
+ */
+int rd_tree_attention_paged(int dtype, const void *q, const void *k_new, const void *v_new,
+                            const void *k_pages, const void *v_pages, int64_t num_pages,
+                            int page_size, const int32_t *block_table, int max_pages,
+                            const int32_t *kv_len, const uint32_t *mask, const int32_t *packed_len,
+                            int B, int P_max, int Hq, int Hkv, int D, float scale,
+                            void *out, void *ws, size_t ws_bytes, rd_stream_t stream);
+
 /* Bytes of device workspace rd_lm_head_argmax needs for these sizes. */
 size_t rd_lm_head_workspace_size(int dtype, int B, int P_max, int K, int V);
 

@@ -1,0 +1,157 @@
+"""GPU parity of tree attention over a paged KV cache (rd_tree_attention_paged).
+
+Pools are cut from a contiguous cache (torch reshapes) and their pages
+permuted at random, with extra unreferenced pages and table entries past
+each cache length set to -1 (never read).  Where the contiguous kernel
+walks the same key order (one split), the paged result must equal
+rd_tree_attention's bit for bit; everywhere it must match the oracle's
+paged attention to the usual normwise tolerance.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verification_rd_amd as rd
+from synthetic import get_config, base_seed
+from harness import Problem, TOL, normwise_rows, to_np, fmt_err
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    rd.load_library()
+
+
+def make_pool(k_cache, v_cache, kv_len, ps, seed, extra=3):
+    """Permuted page pools holding the contiguous caches, and their block table."""
+    B, Hkv, S, D = k_cache.shape
+    n = (S + ps - 1) // ps
+    Sp = n * ps
+    if Sp != S:
+        pad = (0, 0, 0, Sp - S)
+        k_cache = torch.nn.functional.pad(k_cache, pad)
+        v_cache = torch.nn.functional.pad(v_cache, pad)
+
+    def cut(c):
+        return c.reshape(B, Hkv, n, ps, D).permute(0, 2, 1, 3, 4).reshape(B * n, Hkv, ps, D)
+
+    kp, vp = cut(k_cache), cut(v_cache)
+    g = torch.Generator()
+    g.manual_seed(seed)
+    total = B * n + extra
+    perm = torch.randperm(total, generator=g)[: B * n]     # new slot of page i
+    k_pool = torch.randn((total, Hkv, ps, D), device=k_cache.device).to(k_cache.dtype) * 100
+    v_pool = torch.randn((total, Hkv, ps, D), device=k_cache.device).to(k_cache.dtype) * 100
+    k_pool[perm.to(k_cache.device)] = kp
+    v_pool[perm.to(k_cache.device)] = vp
+    table = perm.reshape(B, n).to(torch.int32).clone()
+    kl = kv_len.cpu().numpy()
+    for b in range(B):
+        table[b, (int(kl[b]) + ps - 1) // ps:] = -1
+    return k_pool.contiguous(), v_pool.contiguous(), table.to(k_cache.device)
+
+
+def oracle_paged(prob_q, k_new, v_new, k_pool, v_pool, table, kv_len, mask_t, plen_t):
+    """The oracle's paged attention on the device inputs (fp64 copies)."""
+    B = prob_q.shape[0]
+    mask_bits = mask_t.cpu().numpy().view(np.uint32)
+    P = prob_q.shape[1]
+    mask = np.zeros((B, P, P), bool)
+    for q in range(P):
+        mask[:, :, q] = (mask_bits[:, :, q // 32] >> (q % 32)) & 1
+    return oracle.attention_paged(to_np(prob_q), to_np(k_new), to_np(v_new), to_np(k_pool), to_np(v_pool),
+                                  table.cpu().numpy(), kv_len.cpu().numpy(), mask, plen_t.cpu().numpy())
+
+
+SMALL = {
+    # name: (config overrides, page sizes, kv lengths)
+    "mha_d128": (dict(name="llama_mha", B=3, W=4, L=4, Hq=4, Hkv=4, S=256), (64, 128), [256, 100, 0]),
+    "gqa_d128": (dict(name="gqa", B=2, W=5, L=3, Hq=8, Hkv=2, S=320), (64,), [320, 129]),
+    "mha_d64": (dict(name="llama_mha", B=2, W=3, L=5, Hq=2, Hkv=2, D=64, S=192), (64, 192), [191, 64]),
+    "f32": (dict(name="tiny_f32", B=3, W=4, L=4, S=60), (1, 7, 16, 60), [60, 23, 1]),
+    "split": (dict(name="gqa", B=1, W=4, L=4, Hq=4, Hkv=1, S=4096), (64, 256), [4096]),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_paged_small(name):
+    over, page_sizes, kvl = SMALL[name]
+    over = dict(over)
+    base = get_config(over.pop("name")).with_(**over)
+    prob = Problem(base, base_seed(base, 4), kv_len=np.array(kvl, np.int32))
+    pk = rd.rd_pack_beams(prob.beams_t)
+    mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+    ref = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t, mask,
+                               pk["length"])
+    for ps in page_sizes:
+        k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, ps, seed=ps)
+        got = rd.rd_tree_attention_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, prob.kv_len_t,
+                                         mask, pk["length"])
+        torch.cuda.synchronize()
+        plan_split = name == "split"
+        if not plan_split:
+            assert torch.equal(got, ref), f"{name} ps={ps}: paged differs from contiguous"
+        want = oracle_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, prob.kv_len_t, mask,
+                            pk["length"])
+        plen = pk["length"].cpu().numpy()
+        errs = np.concatenate([normwise_rows(to_np(got[b, :plen[b]]), want[b, :plen[b]]).ravel()
+                               for b in range(base.B)])
+        say(f"[paged] {name} ps={ps}: oracle normwise error {fmt_err(errs)}")
+        assert errs.max() <= TOL[base.dtype]
+        for b in range(base.B):
+            assert (got[b, plen[b]:] == 0).all()
+
+
+@pytest.mark.parametrize("name,split_exact", [("llama_mha", True), ("long_ctx", False)])
+def test_paged_full_size(name, split_exact):
+    """The bench's workloads: paged (64-token pages, permuted pool) against the contiguous call."""
+    cfg = get_config(name)
+    prob = Problem(cfg, base_seed(cfg), checked=[0])
+    pk = rd.rd_pack_beams(prob.beams_t)
+    mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+    ref = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t, mask,
+                               pk["length"])
+    k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, 64, seed=1)
+    got = rd.rd_tree_attention_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, prob.kv_len_t, mask,
+                                     pk["length"])
+    torch.cuda.synchronize()
+    if split_exact:
+        assert torch.equal(got, ref)
+    else:
+        # several splits: the contiguous kernel strides its cache tiles, the paged one does not, so the
+        # summation order differs; both are compared per row
+        plen = pk["length"].cpu().numpy()
+        errs = np.concatenate([normwise_rows(to_np(got[b, :plen[b]]), to_np(ref[b, :plen[b]])).ravel()
+                               for b in range(cfg.B)])
+        say(f"[paged] {name}: paged vs contiguous normwise {fmt_err(errs)}")
+        assert errs.max() <= TOL[cfg.dtype]
+    # request 0 against the oracle, through the paged definition
+    ref0 = prob.oracle_attention()[0]
+    un = pk["unpacker"].cpu().numpy()[0]
+    err = normwise_rows(to_np(got[0])[un], ref0).max()
+    say(f"[paged] {name}: request 0 vs oracle normwise {err:.3e}")
+    assert err <= TOL[cfg.dtype]
+
+
+def test_paged_invalid_arguments():
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((2, 2, 32, 128), dtype=torch.bfloat16, device="cuda")   # 32-token pages: not for bf16
+    table = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    kvl = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    mask = torch.zeros((1, 4, 1), dtype=torch.int32, device="cuda")
+    plen = torch.ones((1,), dtype=torch.int32, device="cuda")
+    with pytest.raises(rd.RdError) as ei:
+        rd.rd_tree_attention_paged(q, kv, kv, pool, pool, table, kvl, mask, plen)
+    assert ei.value.code == -2

@@ -70,6 +70,16 @@ def test_host_side_validation_without_device():
     assert lib.rd_tree_attention(1, *args, 2, 8, 6, 4, 128, 64, 0.0, fake, fake, 0, null) == -1
     assert lib.rd_tree_attention(1, *args, 2, 8, 4, 4, 128, 64, -1.0, fake, fake, 0, null) == -1
     assert lib.rd_tree_attention(1, *args, 0, 8, 4, 4, 128, 64, 0.0, fake, fake, 0, null) == 0
+    # paged attention: bf16 pages must hold whole 64-key tiles; bad page size; empty batch
+    pa = [fake] * 5  # q, k_new, v_new, k_pages, v_pages
+    assert lib.rd_tree_attention_paged(1, *pa, 8, 32, fake, 4, fake, fake, fake, 2, 8, 4, 4, 128, 0.0, fake, fake,
+                                       1 << 20, null) == -2
+    assert lib.rd_tree_attention_paged(1, *pa, 8, 0, fake, 4, fake, fake, fake, 2, 8, 4, 4, 128, 0.0, fake, fake,
+                                       1 << 20, null) == -1
+    assert lib.rd_tree_attention_paged(1, *pa, 8, 64, null, 4, fake, fake, fake, 2, 8, 4, 4, 128, 0.0, fake, fake,
+                                       1 << 20, null) == -1
+    assert lib.rd_tree_attention_paged(1, *pa, 8, 64, fake, 4, fake, fake, fake, 0, 8, 4, 4, 128, 0.0, fake, fake,
+                                       0, null) == 0
     # projection: K not a multiple of 8 in bf16, unknown dtype, empty
     assert lib.rd_lm_head_argmax(1, fake, fake, fake, 2, 8, 100, 50, fake, fake, fake, 1 << 20, null) == -2
     assert lib.rd_lm_head_argmax(5, fake, fake, fake, 2, 8, 128, 50, fake, fake, fake, 1 << 20, null) == -2

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
-    "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_tree_attention", "rd_tree_attention_workspace_size",
+    "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_tree_attention", "rd_tree_attention_paged", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "verify_step",
     "VerifyBuffers",
 ]
@@ -27,7 +27,7 @@ MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 
 EXPORTED_SYMBOLS = (
     "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask",
-    "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_lm_head_workspace_size",
+    "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted",
 )
 
@@ -65,6 +65,8 @@ def load_library():
         "rd_tree_attention_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "rd_tree_attention": ([i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                vp, vp, sz, vp], i32),
+        "rd_tree_attention_paged": ([i32, vp, vp, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     f32, vp, vp, sz, vp], i32),
         "rd_lm_head_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "rd_lm_head_argmax": ([i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
@@ -210,6 +212,41 @@ def rd_tree_attention(q, k_new, v_new, k_cache, v_cache, kv_len, mask, packed_le
     _check(lib.rd_tree_attention(dt, _p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), _p(kv_len), _p(mask),
                                  _p(packed_len), B, P, Hq, Hkv, D, S, float(scale), _p(out), _p(workspace),
                                  workspace.numel(), _stream(q)), "rd_tree_attention")
+    return out
+
+
+def rd_tree_attention_paged(q, k_new, v_new, k_pages, v_pages, block_table, kv_len, mask, packed_len, *,
+                            scale: float = 0.0, out=None, workspace=None) -> torch.Tensor:
+    """Step 2 over a paged cache: pools [num_pages, Hkv, page_size, D], block_table [B, max_pages] int32."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    _need(q, "q", q.dtype)
+    B, P, Hq, D = q.shape
+    dev = q.device
+    Hkv = k_new.shape[2]
+    _need(k_new, "k_new", q.dtype, (B, P, Hkv, D), dev)
+    _need(v_new, "v_new", q.dtype, (B, P, Hkv, D), dev)
+    _need(k_pages, "k_pages", q.dtype, None, dev)
+    if k_pages.dim() != 4 or k_pages.shape[1] != Hkv or k_pages.shape[3] != D:
+        raise ValueError("k_pages must be [num_pages, Hkv, page_size, D]")
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[2]
+    _need(v_pages, "v_pages", q.dtype, tuple(k_pages.shape), dev)
+    _need(block_table, "block_table", torch.int32, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    max_pages = block_table.shape[1]
+    _need(kv_len, "kv_len", torch.int32, (B,), dev)
+    _need(mask, "mask", torch.int32, (B, P, (P + 31) // 32), dev)
+    _need(packed_len, "packed_len", torch.int32, (B,), dev)
+    out = _out(out, "out", (B, P, Hq, D), q.dtype, dev)
+    need = rd_tree_attention_workspace_size(dt, B, P, Hq, Hkv, D, max_pages * page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    _check(lib.rd_tree_attention_paged(dt, _p(q), _p(k_new), _p(v_new), _p(k_pages), _p(v_pages), num_pages,
+                                       page_size, _p(block_table), max_pages, _p(kv_len), _p(mask), _p(packed_len),
+                                       B, P, Hq, Hkv, D, float(scale), _p(out), _p(workspace), workspace.numel(),
+                                       _stream(q)), "rd_tree_attention_paged")
     return out
 
 

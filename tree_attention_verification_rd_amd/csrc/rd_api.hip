@@ -117,6 +117,29 @@ int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v
                                            B, P_max, Hq, Hkv, D, S_max, scale, out, ws, as_stream(stream)));
 }
 
+int rd_tree_attention_paged(int dtype, const void *q, const void *k_new, const void *v_new, const void *k_pages,
+                            const void *v_pages, int64_t num_pages, int page_size, const int32_t *block_table,
+                            int max_pages, const int32_t *kv_len, const uint32_t *mask, const int32_t *packed_len,
+                            int B, int P_max, int Hq, int Hkv, int D, float scale, void *out, void *ws,
+                            size_t ws_bytes, rd_stream_t stream) {
+    if (num_pages < 0 || page_size < 1 || max_pages < 0) return RD_E_ARG;
+    const long long S = static_cast<long long>(max_pages) * page_size;
+    if (S > 0x7FFFFFFFLL) return RD_E_UNSUPPORTED;
+    const int chk = attn_check(dtype, B, P_max, Hq, Hkv, D, static_cast<int>(S));
+    if (chk != RD_OK) return chk;
+    if (B == 0 || P_max == 0 || Hq == 0) return RD_OK;
+    if (!q || !k_new || !v_new || !kv_len || !mask || !packed_len || !out) return RD_E_ARG;
+    if (S > 0 && (!k_pages || !v_pages || !block_table || num_pages < 1)) return RD_E_ARG;
+    if (dtype == RD_BF16 && page_size % 64 != 0) return RD_E_UNSUPPORTED;  // a key tile must not cross a page
+    if (!(scale >= 0.f) || !(scale <= 3.4e38f)) return RD_E_ARG;
+    const rd::AttnPlan plan = rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, static_cast<int>(S));
+    if (ws_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && !ws)) return RD_E_WORKSPACE;
+    const rd::PagedKV pk{block_table, max_pages, page_size, num_pages > 0 ? num_pages : 1};
+    return hip_status(rd::launch_attention(dtype, plan, q, k_new, v_new, k_pages, v_pages, kv_len, mask, packed_len,
+                                           B, P_max, Hq, Hkv, D, static_cast<int>(S), scale, out, ws,
+                                           as_stream(stream), &pk));
+}
+
 static int lm_check(int dtype, int B, int P_max, int K, int V) {
     if (B < 0 || P_max < 0 || K < 0 || V < 0) return RD_E_ARG;
     if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;

@@ -57,7 +57,19 @@ struct AttnArgs {
     uint16_t *out;
     float *ws_o;    // [B, Hkv, nsplit, rows_unit, D]
     float2 *ws_ml;  // [B, Hkv, nsplit, rows_unit]
+    // paged cache: k_cache / v_cache are pools [num_pages, Hkv, page_size, D]
+    const int32_t *bt;  // block table [B, max_pages]
+    int max_pages, page_size;
+    int64_t num_pages;
 };
+
+typedef const int32_t __attribute__((address_space(4))) cint32_t;  // read through the scalar cache
+
+// Page of logical cache position t of request b (clamped into the pool).
+__device__ __forceinline__ int64_t page_of(const AttnArgs &a, int b, int t) {
+    const int32_t pg = ((cint32_t *)a.bt)[static_cast<size_t>(b) * a.max_pages + t / a.page_size];
+    return min(max(static_cast<int64_t>(pg), static_cast<int64_t>(0)), a.num_pages - 1);
+}
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -80,7 +92,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
 // q)*16 + (0..15), or, with LI (lane-interleaved, for few rows), rows
 // row0 + (16*qi + j)*NQG + q for lane j, so a handful of rows still gives
 // every query group -- and so every wavefront -- work.
-template <int D, int QPW, int NWAVE, int KSPLIT, int NS, bool LI>
+// With PAGED the cache comes from a page pool: the page size is a multiple
+// of the 64-key tile, so each cache tile lies in one page, and the tile's
+// load resource starts at that page's rows for this KV head.
+template <int D, int QPW, int NWAVE, int KSPLIT, int NS, bool LI, bool PAGED>
 __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     constexpr int NKC = D / 32;              // k-steps over the head dim (QK^T)
     constexpr int NDB = D / 16;              // 16-row blocks of the head dim (PV)
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     // power-of-two strides, do not all address the same offsets.
     const int trot = ncache > 0 ? (b * 7 + g * 3 + qb * 5) % ncache : 0;
     const int nck = c1 - c0;  // cache keys of this split
-    const bool strided = a.nsplit > 1;
+    const bool strided = !PAGED && a.nsplit > 1;
     const int kmul = strided ? ncache : 1;  // pos(j) = ic*kblk + kmul*j
     const int kblk = strided ? 1 : kBlockN;
     // Load j = NWAVE*jj + wave of an operand covers tile keys KPL*j .. +KPL-1;
@@ -189,20 +204,31 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     const int lslot = lane % KCH;
     auto issue_tile = [&](int i, int slot) {
         const bool cache = i < ncache;
-        const i32x4_t rk = cache ? rk_c : rk_n;
-        const i32x4_t rv = cache ? rv_c : rv_n;
+        i32x4_t rk = cache ? rk_c : rk_n;
+        i32x4_t rv = cache ? rv_c : rv_n;
         const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
         const int kbase = cache ? c0 + ic * kblk : (i - ncache) * kBlockN;
         const int kstep = cache ? kmul : 1;
         const int klim = (i >= ntile) ? 0 : (cache ? c1 : tok_hi);
         const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
         const uint32_t kdst = lds0 + slot * STAGEB;
+        int kres = 0;  // key at the resource base
+        if constexpr (PAGED) {
+            if (cache) {
+                const int64_t pg = page_of(a, b, kbase);
+                const size_t e0 = ((static_cast<size_t>(pg) * a.Hkv + g) * a.page_size + kbase % a.page_size) * D;
+                rk = make_srsrc(a.k_cache + e0, TILEB);
+                rv = make_srsrc(a.v_cache + e0, TILEB);
+                kres = kbase;
+            }
+        }
 #pragma unroll
         for (int jj = 0; jj < NLD; ++jj) {
             const int j = NWAVE * jj + wave;
             const int kl = KPL * j + lkey;
             const int key = kbase + kstep * kl;
-            const uint32_t off = key < klim ? static_cast<uint32_t>(key) * rowstride + ((lslot ^ (kl & 7)) << 4) : kOOB;
+            const uint32_t off =
+                key < klim ? static_cast<uint32_t>(key - kres) * rowstride + ((lslot ^ (kl & 7)) << 4) : kOOB;
             lds_dma16(kdst + j * 1024, rk, off);
             lds_dma16(kdst + TILEB + j * 1024, rv, off);
         }
@@ -550,7 +576,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
 // fp32 path: one wavefront per (request, packed token, head); every lane
 // runs an online softmax over a strided subset of the visible keys, then
 // the 64 partial states are merged through LDS.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void k_tree_attn_f32(const float *__restrict__ q, const float *__restrict__ k_new,
                                                       const float *__restrict__ v_new,
                                                       const float *__restrict__ k_cache,
@@ -559,7 +585,7 @@ __global__ __launch_bounds__(64) void k_tree_attn_f32(const float *__restrict__ 
                                                       const uint32_t *__restrict__ mask,
                                                       const int32_t *__restrict__ plen, int P, int Hq,
                                                       int Hkv, int S_max, int nw, float scale_log2,
-                                                      float *__restrict__ out) {
+                                                      float *__restrict__ out, AttnArgs pg) {
     __shared__ float qs[D];
     __shared__ float part[kWave][D + 1];
     __shared__ float ml[kWave][2];
@@ -588,8 +614,18 @@ __global__ __launch_bounds__(64) void k_tree_attn_f32(const float *__restrict__ 
     for (int j = lane; j < kvl + Pb; j += kWave) {
         const float *kr, *vr;
         if (j < kvl) {
-            kr = k_cache + ((static_cast<size_t>(b) * Hkv + g) * S_max + j) * D;
-            vr = v_cache + ((static_cast<size_t>(b) * Hkv + g) * S_max + j) * D;
+            size_t row;
+            if constexpr (PAGED) {
+                const int64_t page = min(max(static_cast<int64_t>(pg.bt[static_cast<size_t>(b) * pg.max_pages +
+                                                                       j / pg.page_size]),
+                                             static_cast<int64_t>(0)),
+                                         pg.num_pages - 1);
+                row = (static_cast<size_t>(page) * Hkv + g) * pg.page_size + j % pg.page_size;
+            } else {
+                row = (static_cast<size_t>(b) * Hkv + g) * S_max + j;
+            }
+            kr = k_cache + row * D;
+            vr = v_cache + row * D;
         } else {
             const int pk = j - kvl;
             if (!((mrow[pk >> 5] >> (pk & 31)) & 1u)) continue;
@@ -679,19 +715,26 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
                             const void *v_new, const void *k_cache, const void *v_cache,
                             const int32_t *kv_len, const uint32_t *mask, const int32_t *plen, int B,
                             int P_max, int Hq, int Hkv, int D, int S_max, float scale, void *out,
-                            void *ws, hipStream_t stream) {
+                            void *ws, hipStream_t stream, const PagedKV *paged) {
     const float sc = (scale == 0.f) ? 1.f / sqrtf(static_cast<float>(D)) : scale;
     const int nw = (P_max + 31) / 32;
+    AttnArgs a{};
+    if (paged) {
+        a.bt = paged->block_table;
+        a.max_pages = paged->max_pages;
+        a.page_size = paged->page_size;
+        a.num_pages = paged->num_pages;
+    }
     if (dtype == 0) {
         const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * P_max * Hq));
-        auto kern = (D == 64) ? k_tree_attn_f32<64> : k_tree_attn_f32<128>;
+        auto kern = paged ? ((D == 64) ? k_tree_attn_f32<64, true> : k_tree_attn_f32<128, true>)
+                          : ((D == 64) ? k_tree_attn_f32<64, false> : k_tree_attn_f32<128, false>);
         hipLaunchKernelGGL(kern, grid, dim3(kWave), 0, stream, static_cast<const float *>(q),
                            static_cast<const float *>(k_new), static_cast<const float *>(v_new),
                            static_cast<const float *>(k_cache), static_cast<const float *>(v_cache), kv_len,
-                           mask, plen, P_max, Hq, Hkv, S_max, nw, sc * kLog2e, static_cast<float *>(out));
+                           mask, plen, P_max, Hq, Hkv, S_max, nw, sc * kLog2e, static_cast<float *>(out), a);
         return hipGetLastError();
     }
-    AttnArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k_new = static_cast<const uint16_t *>(k_new);
     a.v_new = static_cast<const uint16_t *>(v_new);
@@ -720,21 +763,28 @@ hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, cons
     const dim3 blk(64 * plan.nwave);
     // ring depth: three stages (measured on MI355X: two starve the MFMA-heavy
     // shapes, four did not stream faster)
-    auto go = [&](auto d_c) {
+    auto go = [&](auto d_c, auto pg_c) {
         constexpr int DD = decltype(d_c)::value;
+        constexpr bool PG = decltype(pg_c)::value;
         if (plan.ksplit == 2 && plan.qpw == 1)
-            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 1, 8, 2, 3, true>), grid, blk, 0, stream, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 1, 8, 2, 3, true, PG>), grid, blk, 0, stream, a);
         else if (plan.ksplit == 2)
-            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 2, 3, false>), grid, blk, 0, stream, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 2, 3, false, PG>), grid, blk, 0, stream, a);
         else if (plan.nwave == 4)
-            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 1, 3, false>), grid, blk, 0, stream, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 4, 1, 3, false, PG>), grid, blk, 0, stream, a);
         else
-            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 8, 1, 3, false>), grid, blk, 0, stream, a);
+            hipLaunchKernelGGL((k_tree_attn_bf16<DD, 2, 8, 1, 3, false, PG>), grid, blk, 0, stream, a);
     };
-    if (D == 64)
-        go(std::integral_constant<int, 64>{});
+    auto go_d = [&](auto pg_c) {
+        if (D == 64)
+            go(std::integral_constant<int, 64>{}, pg_c);
+        else
+            go(std::integral_constant<int, 128>{}, pg_c);
+    };
+    if (paged)
+        go_d(std::true_type{});
     else
-        go(std::integral_constant<int, 128>{});
+        go_d(std::false_type{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || plan.nsplit == 1) return err;
     const unsigned ncomb = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * (plan.rows_unit / kCombRows));

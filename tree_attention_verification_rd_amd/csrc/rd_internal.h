@@ -30,11 +30,18 @@ struct AttnPlan {
     int ksplit;     // wavefronts sharing one query block's keys of a tile (1 or 2)
 };
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max);
+// paged cache: pools [num_pages, Hkv, page_size, D], block table [B, max_pages]
+struct PagedKV {
+    const int32_t *block_table;
+    int max_pages, page_size;
+    int64_t num_pages;
+};
+// paged != nullptr: k_cache / v_cache are the pools and S_max = max_pages * page_size
 hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *k_new,
                             const void *v_new, const void *k_cache, const void *v_cache,
                             const int32_t *kv_len, const uint32_t *mask, const int32_t *plen,
                             int B, int P_max, int Hq, int Hkv, int D, int S_max, float scale,
-                            void *out, void *ws, hipStream_t stream);
+                            void *out, void *ws, hipStream_t stream, const PagedKV *paged = nullptr);
 
 // output projection + argmax
 struct LmPlan {
