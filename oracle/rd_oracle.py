@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "pack_beams", "tree_mask", "mask_to_bits", "attention_per_beam",
     "attention_packed", "gather_pages", "attention_paged", "lm_head_logits", "argmax_first", "unpack",
-    "greedy_accept", "commit_accepted", "verify_requests",
+    "greedy_accept", "commit_accepted", "commit_accepted_paged", "verify_requests",
 ]
 
 
@@ -358,6 +358,37 @@ def commit_accepted(k, v, hidden, best_beam, accept_len, k_cache, v_cache, kv_le
         committed[b] = True
         hidden_next[b] = hidden[b, w, n]
     return {"k_cache": kc, "v_cache": vc, "kv_len": new_len, "committed": committed,
+            "hidden_next": hidden_next}
+
+
+def commit_accepted_paged(k, v, hidden, best_beam, accept_len, k_pages, v_pages, block_table, kv_len) -> dict:
+    """commit_accepted into a paged cache (pools and table as in gather_pages).
+
+    Logical position t of request b is row t % page_size of page
+    block_table[b, t // page_size]; the capacity is max_pages * page_size.
+    Same rows, same hidden state, same overflow rule as commit_accepted.
+    """
+    B, W, L = np.asarray(k).shape[:3]
+    ps = k_pages.shape[2]
+    cap = block_table.shape[1] * ps
+    kp = np.array(k_pages, np.float64)
+    vp = np.array(v_pages, np.float64)
+    new_len = np.array(kv_len, np.int32)
+    committed = np.zeros(B, bool)
+    hidden_next = np.full((B, np.asarray(hidden).shape[3]), np.nan)
+    for b in range(B):
+        w, n, c = int(best_beam[b]), int(accept_len[b]), int(kv_len[b])
+        if not (0 <= w < W and 0 <= n <= L - 1 and 0 <= c and c + n + 1 <= cap):
+            continue
+        for j in range(n + 1):
+            t = c + j
+            page = int(block_table[b, t // ps])
+            kp[page, :, t % ps] = k[b, w, j]
+            vp[page, :, t % ps] = v[b, w, j]
+        new_len[b] = c + n + 1
+        committed[b] = True
+        hidden_next[b] = hidden[b, w, n]
+    return {"k_pages": kp, "v_pages": vp, "kv_len": new_len, "committed": committed,
             "hidden_next": hidden_next}
 
 

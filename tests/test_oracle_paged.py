@@ -90,3 +90,33 @@ def test_shared_prefix_pages():
     kp[own], vp[own] = 1e3, -1e3                  # its own first pages, no longer referenced
     got = oracle.attention_paged(pq["q"], pq["k"], pq["v"], kp, vp, table, kv_len, mask, plen)
     np.testing.assert_array_equal(got, ref)
+
+
+def test_paged_commit_equals_contiguous_commit_through_the_gather():
+    """Committing into pages, then gathering, equals committing into the gathered cache."""
+    cfg = get_config("tiny_f32").with_(B=3, W=4, L=5, S=40, Hq=4, Hkv=2, D=8)
+    beams = draw_beams(cfg, 12)
+    nodes = unpacked_node_tensors(cfg, 12, beams)
+    kc = np.zeros((cfg.B, cfg.Hkv, cfg.S, cfg.D), np.float32)
+    vc = np.zeros_like(kc)
+    for b in range(cfg.B):
+        kc[b], vc[b] = kv_cache(cfg, 12, b)
+    ps = 8
+    kp, table = pool_from_cache(kc, ps)
+    vp, _ = pool_from_cache(vc, ps)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(kp.shape[0])
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    table = perm[table].astype(np.int32)
+    kv_len = np.array([13, 0, 36], np.int32)          # request 2 overflows with more than 3 rows
+    best = np.array([1, 3, 2], np.int32)
+    n_acc = np.array([4, 2, 4], np.int32)
+    got = oracle.commit_accepted_paged(nodes["k"], nodes["v"], nodes["hidden"], best, n_acc, kp2, vp2, table, kv_len)
+    ref = oracle.commit_accepted(nodes["k"], nodes["v"], nodes["hidden"], best, n_acc, kc, vc, kv_len)
+    np.testing.assert_array_equal(got["kv_len"], ref["kv_len"])
+    np.testing.assert_array_equal(got["committed"], [True, True, False])
+    np.testing.assert_array_equal(got["hidden_next"], ref["hidden_next"])
+    full = np.full(cfg.B, cfg.S, np.int32)
+    np.testing.assert_array_equal(oracle.gather_pages(got["k_pages"], table, full), ref["k_cache"])
+    np.testing.assert_array_equal(oracle.gather_pages(got["v_pages"], table, full), ref["v_cache"])
