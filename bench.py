@@ -298,6 +298,14 @@ def main():
                                    out=paged_out, workspace=paged_ws)
 
     paged_us = queued_call_us(paged_call, lambda: None)
+
+    def commit_paged_call(i):
+        s = sets[i % n_sets]
+        kp, vp, tbl = pools[i % n_sets]
+        rd.rd_commit_accepted_paged(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], kp, vp, tbl, c_kv[i],
+                                    s["hidden"], hidden_next=c_hid)
+
+    commit_paged_us = queued_call_us(commit_paged_call, lambda: c_kv.fill_(cfg.S - cfg.L))
     contig_us = queued_call_us(lambda i: rd.rd_tree_attention(
         sets[i % n_sets]["q"], sets[i % n_sets]["k_new"], sets[i % n_sets]["v_new"], sets[i % n_sets]["k_cache"],
         sets[i % n_sets]["v_cache"], kv_len, bufs.mask, pk["length"], out=paged_out, workspace=bufs.attn_ws),
@@ -346,7 +354,7 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "gpu_ms_per_step": round(ms_gpu, 4),
         "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
-                       "bytes_moved": int(commit_bytes)},
+                       "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
         "attention_paged": {"call": "rd_tree_attention_paged", "page_size": ps, "avg_us": round(paged_us, 2),
                             "contiguous_avg_us": round(contig_us, 2),
                             "achieved": round(work["attention"][0] / (paged_us * 1e-6) / 1e9, 1),

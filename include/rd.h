@@ -266,6 +266,26 @@ int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_b
                        int S_max, void *k_cache, void *v_cache, int32_t *kv_len,
                        void *hidden_next, rd_stream_t stream);
 
+/*
+ * rd_commit_accepted into a paged cache (pools and block table as for
+ * rd_tree_attention_paged): logical position t = kv_len[b] + j goes to row
+ * t % page_size of page block_table[b, t / page_size]; the capacity is
+ * max_pages * page_size.  The caller gives every request table entries for
+ * the positions it may commit; page ids are clamped to [0, num_pages).
+ * Same rows, hidden state, overflow rule, launch count and errors as
+ * rd_commit_accepted, plus RD_E_ARG for page_size < 1, negative num_pages
+ * or max_pages, or a null pool or table.
+ *
+ *   k_pages, v_pages (dev) [num_pages, Hkv, page_size, D] in dtype, updated in place
+ *   block_table (dev) int32 [B, max_pages]
+ */
+int rd_commit_accepted_paged(int dtype, const int32_t *unpacker, const int32_t *best_beam,
+                             const int32_t *accept_len, const void *k_new, const void *v_new,
+                             const void *hidden, int B, int W, int L, int Hkv, int D, int K,
+                             void *k_pages, void *v_pages, int64_t num_pages, int page_size,
+                             const int32_t *block_table, int max_pages, int32_t *kv_len,
+                             void *hidden_next, rd_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def need_gpu():
     rd.load_library()
 
 
-def make_pool(k_cache, v_cache, kv_len, ps, seed, extra=3):
+def make_pool(k_cache, v_cache, kv_len, ps, seed, extra=3, unread_to_minus_one=True):
     """Permuted page pools holding the contiguous caches, and their block table."""
     B, Hkv, S, D = k_cache.shape
     n = (S + ps - 1) // ps
@@ -57,9 +57,19 @@ def make_pool(k_cache, v_cache, kv_len, ps, seed, extra=3):
     v_pool[perm.to(k_cache.device)] = vp
     table = perm.reshape(B, n).to(torch.int32).clone()
     kl = kv_len.cpu().numpy()
-    for b in range(B):
-        table[b, (int(kl[b]) + ps - 1) // ps:] = -1
+    if unread_to_minus_one:
+        for b in range(B):
+            table[b, (int(kl[b]) + ps - 1) // ps:] = -1
     return k_pool.contiguous(), v_pool.contiguous(), table.to(k_cache.device)
+
+
+def logical_from_pool(pool, table, S):
+    """[B, Hkv, S, D] view of the pool through the table (torch indexing)."""
+    B, n = table.shape
+    ps = pool.shape[2]
+    rows = pool[table.long().reshape(-1)]                         # [B*n, Hkv, ps, D]
+    rows = rows.reshape(B, n, pool.shape[1], ps, pool.shape[3]).permute(0, 2, 1, 3, 4)
+    return rows.reshape(B, pool.shape[1], n * ps, pool.shape[3])[:, :, :S]
 
 
 def oracle_paged(prob_q, k_new, v_new, k_pool, v_pool, table, kv_len, mask_t, plen_t):
@@ -155,3 +165,43 @@ def test_paged_invalid_arguments():
     with pytest.raises(rd.RdError) as ei:
         rd.rd_tree_attention_paged(q, kv, kv, pool, pool, table, kvl, mask, plen)
     assert ei.value.code == -2
+
+
+@pytest.mark.parametrize("name,ps", [("llama_mha", 64), ("gqa", 128), ("tiny_f32", 7)])
+def test_paged_commit_then_attention(name, ps):
+    """Paged commit equals the contiguous commit; the next step's paged attention sees the same cache."""
+    # S is a multiple of the page size, so both caches hold the same number of positions
+    over = {"llama_mha": dict(B=4, S=256), "gqa": dict(B=3, S=384), "tiny_f32": dict(B=3, S=42)}[name]
+    cfg = get_config(name).with_(**over)
+    kv = np.array([0, cfg.S - cfg.L] + [37] * (cfg.B - 3) + [cfg.S], np.int32)   # the last one overflows
+    prob = Problem(cfg, base_seed(cfg, 2), plant=True, kv_len=kv)
+    res = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t,
+                         prob.hidden, prob.weight, want_logits=False)
+    un, best, nacc = res["pack"]["unpacker"], res["best_beam"], res["accept_len"]
+    k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, ps, seed=5,
+                                      unread_to_minus_one=False)
+    untouched = [i for i in range(k_pool.shape[0]) if i not in set(table.cpu().numpy().ravel().tolist())]
+    spare_k, spare_v = k_pool[untouched].clone(), v_pool[untouched].clone()
+    kv_c, kv_p = prob.kv_len_t.clone(), prob.kv_len_t.clone()
+    h_c = rd.rd_commit_accepted(un, best, nacc, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, kv_c,
+                                prob.hidden)
+    h_p = rd.rd_commit_accepted_paged(un, best, nacc, prob.k_new, prob.v_new, k_pool, v_pool, table, kv_p,
+                                      prob.hidden)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_p, kv_c)
+    moved = (kv_c != prob.kv_len_t).cpu().numpy()
+    assert moved[0] and not moved[-1]
+    for b in np.nonzero(moved)[0]:
+        assert torch.equal(h_p[b], h_c[b])
+    assert torch.equal(logical_from_pool(k_pool, table, cfg.S), prob.k_cache)
+    assert torch.equal(logical_from_pool(v_pool, table, cfg.S), prob.v_cache)
+    assert torch.equal(k_pool[untouched], spare_k) and torch.equal(v_pool[untouched], spare_v)
+    # next step over the grown caches: paged and contiguous attention agree bit for bit
+    pk = rd.rd_pack_beams(prob.beams_t)
+    mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+    a_c = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, kv_c, mask, pk["length"])
+    a_p = rd.rd_tree_attention_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, kv_p, mask,
+                                     pk["length"])
+    torch.cuda.synchronize()
+    assert torch.equal(a_p, a_c)
+    say(f"[paged] commit {name} ps={ps}: {int(moved.sum())}/{cfg.B} committed, exact")

@@ -96,6 +96,13 @@ def test_host_side_validation_without_device():
     assert lib.rd_commit_accepted(1, *c, 2, 8, 5, 32, 128, 4096, -1, *o, null) == -1
     assert lib.rd_commit_accepted(3, *c, 2, 8, 5, 32, 128, 4096, 1024, *o, null) == -2
     assert lib.rd_commit_accepted(1, *c, 2, 8, 17, 32, 128, 4096, 1024, *o, null) == -2
+    # paged commit: page size 0, null table, unknown dtype
+    assert lib.rd_commit_accepted_paged(1, *c, 2, 8, 5, 32, 128, 4096, fake, fake, 16, 0, fake, 4, fake, fake,
+                                        null) == -1
+    assert lib.rd_commit_accepted_paged(1, *c, 2, 8, 5, 32, 128, 4096, fake, fake, 16, 64, null, 4, fake, fake,
+                                        null) == -1
+    assert lib.rd_commit_accepted_paged(4, *c, 2, 8, 5, 32, 128, 4096, fake, fake, 16, 64, fake, 4, fake, fake,
+                                        null) == -2
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

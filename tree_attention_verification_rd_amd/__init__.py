@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
     "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_tree_attention", "rd_tree_attention_paged", "rd_tree_attention_workspace_size",
-    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "verify_step",
+    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "verify_step",
     "VerifyBuffers",
 ]
 
@@ -28,7 +28,7 @@ MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 EXPORTED_SYMBOLS = (
     "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
-    "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted",
+    "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,8 @@ def load_library():
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_commit_accepted": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                 vp], i32),
+        "rd_commit_accepted_paged": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64, i32,
+                                      vp, i32, vp, vp, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -349,6 +351,44 @@ def rd_commit_accepted(unpacker, best_beam, accept_len, k_new, v_new, k_cache, v
     _check(lib.rd_commit_accepted(dt, _p(unpacker), _p(best_beam), _p(accept_len), _p(k_new), _p(v_new), _p(hidden),
                                   B, W, L, Hkv, D, K, S, _p(k_cache), _p(v_cache), _p(kv_len), _p(hidden_next),
                                   _stream(unpacker)), "rd_commit_accepted")
+    return hidden_next
+
+
+def rd_commit_accepted_paged(unpacker, best_beam, accept_len, k_new, v_new, k_pages, v_pages, block_table, kv_len,
+                             hidden=None, *, hidden_next=None):
+    """rd_commit_accepted into paged pools [num_pages, Hkv, page_size, D] through block_table [B, max_pages]."""
+    lib = load_library()
+    _need(unpacker, "unpacker", torch.int32)
+    B, W, L = unpacker.shape
+    dev = unpacker.device
+    dt = _dtype_code(k_new)
+    _need(k_new, "k_new", k_new.dtype, None, dev)
+    if k_new.dim() != 4 or k_new.shape[0] != B or k_new.shape[1] != W * L:
+        raise ValueError("k_new must be [B, W*L, Hkv, D]")
+    Hkv, D = k_new.shape[2], k_new.shape[3]
+    _need(v_new, "v_new", k_new.dtype, (B, W * L, Hkv, D), dev)
+    _need(k_pages, "k_pages", k_new.dtype, None, dev)
+    if k_pages.dim() != 4 or k_pages.shape[1] != Hkv or k_pages.shape[3] != D:
+        raise ValueError("k_pages must be [num_pages, Hkv, page_size, D]")
+    _need(v_pages, "v_pages", k_new.dtype, tuple(k_pages.shape), dev)
+    _need(block_table, "block_table", torch.int32, None, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    for t, name in ((best_beam, "best_beam"), (accept_len, "accept_len"), (kv_len, "kv_len")):
+        _need(t, name, torch.int32, (B,), dev)
+    K = 0
+    if hidden is not None:
+        _need(hidden, "hidden", k_new.dtype, None, dev)
+        if hidden.dim() != 3 or tuple(hidden.shape[:2]) != (B, W * L):
+            raise ValueError("hidden must be [B, W*L, K]")
+        K = hidden.shape[2]
+        hidden_next = _out(hidden_next, "hidden_next", (B, K), k_new.dtype, dev)
+    else:
+        hidden_next = None
+    _check(lib.rd_commit_accepted_paged(dt, _p(unpacker), _p(best_beam), _p(accept_len), _p(k_new), _p(v_new),
+                                        _p(hidden), B, W, L, Hkv, D, K, _p(k_pages), _p(v_pages), k_pages.shape[0],
+                                        k_pages.shape[2], _p(block_table), block_table.shape[1], _p(kv_len),
+                                        _p(hidden_next), _stream(unpacker)), "rd_commit_accepted_paged")
     return hidden_next
 
 

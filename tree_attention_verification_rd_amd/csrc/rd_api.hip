@@ -213,4 +213,29 @@ int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_b
                                         as_stream(stream)));
 }
 
+int rd_commit_accepted_paged(int dtype, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,
+                             const void *k_new, const void *v_new, const void *hidden, int B, int W, int L, int Hkv,
+                             int D, int K, void *k_pages, void *v_pages, int64_t num_pages, int page_size,
+                             const int32_t *block_table, int max_pages, int32_t *kv_len, void *hidden_next,
+                             rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L) || Hkv < 1 || D < 1 || K < 0 || num_pages < 0 || page_size < 1 || max_pages < 0)
+        return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!unpacker || !best_beam || !accept_len || !k_new || !v_new || !k_pages || !v_pages || !block_table ||
+        !kv_len || num_pages < 1)
+        return RD_E_ARG;
+    if ((hidden != nullptr) != (hidden_next != nullptr) || (hidden && K < 1)) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    const long long S = static_cast<long long>(max_pages) * page_size;
+    if (S > 0x7FFFFFFFLL) return RD_E_UNSUPPORTED;
+    const int64_t esize = dtype == RD_F32 ? 4 : 2;
+    const int64_t units = (2 * static_cast<int64_t>(Hkv) * L * D + (hidden ? K : 0)) * esize / 2;
+    if (units >= (1LL << 30)) return RD_E_UNSUPPORTED;
+    const rd::PagedKV pk{block_table, max_pages, page_size, num_pages};
+    return hip_status(rd::launch_commit(static_cast<int>(esize), unpacker, best_beam, accept_len, k_new, v_new,
+                                        hidden, B, W, L, Hkv, D, K, static_cast<int>(S), k_pages, v_pages, kv_len,
+                                        hidden_next, as_stream(stream), &pk));
+}
+
 }  // extern "C"

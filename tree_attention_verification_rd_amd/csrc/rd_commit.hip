@@ -17,6 +17,10 @@ struct CommitArgs {
     int W, L, P, Hkv, S;
     int row_units;  // copy units per key/value row (one KV head of one token)
     int hid_units;  // copy units per hidden row, 0 when no hidden row is picked
+    // paged cache: k_cache / v_cache are pools [num_pages, Hkv, page_size, D], S = max_pages * page_size
+    const int32_t *bt;  // block table [B, max_pages]
+    int max_pages, page_size;
+    int64_t num_pages;
 };
 
 // One workgroup per request.  Every work item of the request -- the key and
@@ -27,7 +31,9 @@ struct CommitArgs {
 // kv_len[b] is read by every thread before the first barrier and written
 // once by thread 0 after the copies, so it can be advanced in place within
 // the one launch.
-template <typename T, int U>
+// With PAGED, position t goes to row t % page_size of page
+// block_table[b, t / page_size] (clamped into the pool).
+template <typename T, int U, bool PAGED>
 __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
     __shared__ int slot[kMaxBeamLen];
     const int b = blockIdx.x;
@@ -68,7 +74,18 @@ __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
         const int j = r / a.row_units;
         const int u = r - j * a.row_units;
         src = (is_v ? vnew : knew) + ((pbase + slot[j]) * a.Hkv + g) * a.row_units + u;
-        dst = (is_v ? vc : kc) + ((static_cast<size_t>(b) * a.Hkv + g) * a.S + c + j) * a.row_units + u;
+        size_t drow;
+        if constexpr (PAGED) {
+            const int t = c + j;
+            const int64_t pg = min(max(static_cast<int64_t>(a.bt[static_cast<size_t>(b) * a.max_pages +
+                                                                 t / a.page_size]),
+                                       static_cast<int64_t>(0)),
+                                   a.num_pages - 1);
+            drow = (static_cast<size_t>(pg) * a.Hkv + g) * a.page_size + t % a.page_size;
+        } else {
+            drow = (static_cast<size_t>(b) * a.Hkv + g) * a.S + c + j;
+        }
+        dst = (is_v ? vc : kc) + drow * a.row_units + u;
     };
 
     for (int base = threadIdx.x; base < total; base += blockDim.x * U) {
@@ -95,7 +112,7 @@ __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
 hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,
                          const void *k_new, const void *v_new, const void *hidden, int B, int W, int L, int Hkv,
                          int D, int K, int S, void *k_cache, void *v_cache, int32_t *kv_len, void *hidden_next,
-                         hipStream_t stream) {
+                         hipStream_t stream, const PagedKV *paged) {
     const bool with_hidden = hidden && hidden_next && K > 0;
     const int64_t row_bytes = static_cast<int64_t>(D) * esize;
     const int64_t hid_bytes = with_hidden ? static_cast<int64_t>(K) * esize : 0;
@@ -106,12 +123,22 @@ hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best
     const int unit = wide ? 16 : 2;
     CommitArgs a{unpacker, best_beam, accept_len, k_new, v_new, with_hidden ? hidden : nullptr,
                  k_cache, v_cache, with_hidden ? hidden_next : nullptr, kv_len,
-                 W, L, W * L, Hkv, S, static_cast<int>(row_bytes / unit), static_cast<int>(hid_bytes / unit)};
+                 W, L, W * L, Hkv, S, static_cast<int>(row_bytes / unit), static_cast<int>(hid_bytes / unit),
+                 nullptr, 0, 1, 1};
+    if (paged) {
+        a.bt = paged->block_table;
+        a.max_pages = paged->max_pages;
+        a.page_size = paged->page_size;
+        a.num_pages = paged->num_pages;
+    }
     constexpr int U = 4;
-    if (wide)
-        hipLaunchKernelGGL((k_commit<u32x4, U>), dim3(B), dim3(1024), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_commit<uint16_t, U>), dim3(B), dim3(1024), 0, stream, a);
+    if (wide) {
+        auto kern = paged ? k_commit<u32x4, U, true> : k_commit<u32x4, U, false>;
+        hipLaunchKernelGGL(kern, dim3(B), dim3(1024), 0, stream, a);
+    } else {
+        auto kern = paged ? k_commit<uint16_t, U, true> : k_commit<uint16_t, U, false>;
+        hipLaunchKernelGGL(kern, dim3(B), dim3(1024), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

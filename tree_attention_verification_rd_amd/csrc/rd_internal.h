@@ -67,7 +67,7 @@ hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_
 hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,
                          const void *k_new, const void *v_new, const void *hidden, int B, int W, int L, int Hkv,
                          int D, int K, int S, void *k_cache, void *v_cache, int32_t *kv_len, void *hidden_next,
-                         hipStream_t stream);
+                         hipStream_t stream, const PagedKV *paged = nullptr);
 
 int device_cu_count();
 
