@@ -50,7 +50,7 @@ __all__ = [
 
 
 # ---------------------------------------------------------------- step 1 --
-def pack_beams(beams: np.ndarray) -> dict:
+def pack_beams(beams: np.ndarray, beam_width=None, beam_len=None) -> dict:
     """Deduplicate shared prefixes of each request's beams with a literal trie.
 
     [NEWS] "Dynamic tree attention" and [PAPER] abstract (2): the beams that
@@ -66,21 +66,28 @@ def pack_beams(beams: np.ndarray) -> dict:
     Returns int32 arrays: tokens [B,P] (pad -1), length [B], unpacker
     [B,W,L], depth [B,P] (pad -1), src [B,P] = w*L+l of the first
     occurrence (pad -1), with P = W*L.
+
+    Ragged batches ([TRT] "Inflight-batching Compatible Engine": requests in
+    one batch differ).  Reading: request b has beam_width[b] <= W beams of
+    beam_len[b] <= L tokens, stored in the top-left corner of its [W, L]
+    slab; the rest is padding that opens no node and gets unpacker -1.
     """
     beams = np.asarray(beams)
     B, W, L = beams.shape
+    bw = [W] * B if beam_width is None else [min(max(int(x), 0), W) for x in beam_width]
+    bl = [L] * B if beam_len is None else [min(max(int(x), 0), L) for x in beam_len]
     P = W * L
     tokens = np.full((B, P), -1, np.int32)
     depth = np.full((B, P), -1, np.int32)
     src = np.full((B, P), -1, np.int32)
     length = np.zeros(B, np.int32)
-    unpacker = np.zeros((B, W, L), np.int32)
+    unpacker = np.full((B, W, L), -1, np.int32)
     for b in range(B):
         child = {}  # (parent node or -1 for the virtual root, token) -> node
         n = 0
-        for w in range(W):
+        for w in range(bw[b]):
             cur = -1
-            for l in range(L):
+            for l in range(bl[b]):
                 key = (cur, int(beams[b, w, l]))
                 if key not in child:
                     child[key] = n
@@ -101,7 +108,8 @@ def tree_mask(unpacker: np.ndarray, packed_len: np.ndarray) -> np.ndarray:
     depth-first-compatible order and one topology-aware causal mask lets a
     single kernel evaluate every path.  Node p = unpacker[b,w,l] has as
     ancestors-or-self exactly the nodes unpacker[b,w,0..l] on its beam.
-    Rows and columns at or beyond packed_len are zero.
+    Rows and columns at or beyond packed_len are zero; padding candidates
+    (unpacker -1) are skipped.
     """
     B, W, L = unpacker.shape
     P = W * L
@@ -110,6 +118,8 @@ def tree_mask(unpacker: np.ndarray, packed_len: np.ndarray) -> np.ndarray:
         for w in range(W):
             for l in range(L):
                 p = unpacker[b, w, l]
+                if p < 0:
+                    continue
                 for j in range(l + 1):
                     mask[b, p, unpacker[b, w, j]] = True
         n = int(packed_len[b])
@@ -259,21 +269,23 @@ def argmax_first(logits: np.ndarray) -> np.ndarray:
 def unpack(packed: np.ndarray, unpacker: np.ndarray) -> np.ndarray:
     """[TRT] PyTorch `unpack`: out[b,w,l,:] = packed[b, unpacker[b,w,l], :].
 
-    packed [B,P,X] (rank 3), unpacker [B,W,L] -> [B,W,L,X].
+    packed [B,P,X] (rank 3), unpacker [B,W,L] -> [B,W,L,X].  Padding
+    candidates of ragged requests (unpacker -1) get zero rows.
     """
     packed = np.asarray(packed)
     assert packed.ndim == 3
     B, W, L = unpacker.shape
-    out = np.empty((B, W, L, packed.shape[2]), dtype=packed.dtype)
+    out = np.zeros((B, W, L, packed.shape[2]), dtype=packed.dtype)
     for b in range(B):
         for w in range(W):
             for l in range(L):
-                out[b, w, l] = packed[b, unpacker[b, w, l]]
+                if unpacker[b, w, l] >= 0:
+                    out[b, w, l] = packed[b, unpacker[b, w, l]]
     return out
 
 
 # ---------------------------------------------------------------- step 4 --
-def greedy_accept(beams: np.ndarray, target: np.ndarray) -> dict:
+def greedy_accept(beams: np.ndarray, target: np.ndarray, beam_width=None, beam_len=None) -> dict:
     """Greedy acceptance of the best beam plus one bonus token.
 
     [TRT] intro: tokens are verified and the best path is accepted before
@@ -290,17 +302,26 @@ def greedy_accept(beams: np.ndarray, target: np.ndarray) -> dict:
 
     Returns int32: match_len [B,W], best_beam [B], accept_len [B] (= n),
     accepted_tokens [B,L] (n drafts + bonus, pad -1).
+
+    Ragged requests (see pack_beams): only beams w < beam_width[b] and
+    positions below beam_len[b] take part; padding beams get match_len -1,
+    and a request with no beam or no position accepts nothing (best_beam
+    and accept_len -1, accepted_tokens all -1).
     """
     B, W, L = beams.shape
-    match_len = np.zeros((B, W), np.int32)
-    best_beam = np.zeros(B, np.int32)
-    accept_len = np.zeros(B, np.int32)
+    bw = [W] * B if beam_width is None else [min(max(int(x), 0), W) for x in beam_width]
+    bl = [L] * B if beam_len is None else [min(max(int(x), 0), L) for x in beam_len]
+    match_len = np.full((B, W), -1, np.int32)
+    best_beam = np.full(B, -1, np.int32)
+    accept_len = np.full(B, -1, np.int32)
     accepted = np.full((B, L), -1, np.int32)
     for b in range(B):
+        if bw[b] == 0 or bl[b] == 0:
+            continue
         best, best_n = 0, -1
-        for w in range(W):
+        for w in range(bw[b]):
             n = 0
-            while n < L - 1 and beams[b, w, n + 1] == target[b, w, n]:
+            while n < bl[b] - 1 and beams[b, w, n + 1] == target[b, w, n]:
                 n += 1
             match_len[b, w] = n
             if n > best_n:
