@@ -306,6 +306,28 @@ def main():
                                     s["hidden"], hidden_next=c_hid)
 
     commit_paged_us = queued_call_us(commit_paged_call, lambda: c_kv.fill_(cfg.S - cfg.L))
+
+    # Ragged batch: the same beams with seeded per-request beam counts and
+    # lengths (1..W, 1..L), through the two calls whose work depends on them.
+    rng_r = np.random.default_rng(seed + 17)
+    r_bw = torch.from_numpy(rng_r.integers(1, cfg.W + 1, size=B).astype(np.int32)).to(dev)
+    r_bl = torch.from_numpy(rng_r.integers(1, cfg.L + 1, size=B).astype(np.int32)).to(dev)
+    r_pk = {k: torch.empty_like(v) for k, v in pk.items()}
+    r_mask = torch.empty_like(bufs.mask)
+    r_acc = {k: torch.empty_like(v) for k, v in bufs.accept.items()}
+
+    def ragged_pack_call(i):
+        rd.rd_pack_beams_mask(beams, packed_tokens=r_pk["tokens"], packed_len=r_pk["length"],
+                              unpacker=r_pk["unpacker"], packed_depth=r_pk["depth"], packed_src=r_pk["src"],
+                              mask=r_mask, beam_width=r_bw, beam_len=r_bl)
+
+    def ragged_accept_call(i):
+        rd.rd_unpack_accept(beams, r_pk["unpacker"], bufs.argmax, bufs.logits if full else None,
+                            unpacked=bufs.unpacked, beam_width=r_bw, beam_len=r_bl, **r_acc)
+
+    ragged_pack_us = queued_call_us(ragged_pack_call, lambda: None)
+    ragged_accept_us = queued_call_us(ragged_accept_call, lambda: None)
+    ragged_packed = int(r_pk["length"].sum().item())
     contig_us = queued_call_us(lambda i: rd.rd_tree_attention(
         sets[i % n_sets]["q"], sets[i % n_sets]["k_new"], sets[i % n_sets]["v_new"], sets[i % n_sets]["k_cache"],
         sets[i % n_sets]["v_cache"], kv_len, bufs.mask, pk["length"], out=paged_out, workspace=bufs.attn_ws),
@@ -355,6 +377,9 @@ def main():
         "gpu_ms_per_step": round(ms_gpu, 4),
         "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
                        "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
+        "ragged": {"calls": "rd_pack_beams_mask_ragged + rd_unpack_accept_ragged",
+                   "candidates": int((r_bw * r_bl).sum().item()), "packed_tokens": ragged_packed,
+                   "pack_mask_us": round(ragged_pack_us, 2), "unpack_accept_us": round(ragged_accept_us, 2)},
         "attention_paged": {"call": "rd_tree_attention_paged", "page_size": ps, "avg_us": round(paged_us, 2),
                             "contiguous_avg_us": round(contig_us, 2),
                             "achieved": round(work["attention"][0] / (paged_us * 1e-6) / 1e9, 1),

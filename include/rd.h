@@ -126,6 +126,22 @@ int rd_pack_beams_mask(const int32_t *beams, int B, int W, int L,
                        int32_t *packed_depth, int32_t *packed_src, uint32_t *mask,
                        rd_stream_t stream);
 
+/*
+ * Steps 1 + 1b for a ragged batch.  [TRT] "Inflight-batching Compatible
+ * Engine": the requests of one batch differ in shape.  Request b has
+ * beam_width[b] <= W beams of beam_len[b] <= L tokens (dev int32 [B] each,
+ * clamped to [0,W] / [0,L]) in the top-left corner of its [W,L] slab of
+ * beams; the rest is padding.  Padding candidates open no slot and get
+ * unpacker -1; everything else is exactly rd_pack_beams_mask on the request's
+ * [beam_width[b], beam_len[b]] sub-array, with packed_src still w*L+l in the
+ * padded slab.  A request with no beam or no position has packed_len 0.
+ */
+int rd_pack_beams_mask_ragged(const int32_t *beams, const int32_t *beam_width,
+                              const int32_t *beam_len, int B, int W, int L,
+                              int32_t *packed_tokens, int32_t *packed_len, int32_t *unpacker,
+                              int32_t *packed_depth, int32_t *packed_src, uint32_t *mask,
+                              rd_stream_t stream);
+
 /* Bytes of device workspace rd_tree_attention needs for these sizes (may be 0). */
 size_t rd_tree_attention_workspace_size(int dtype, int B, int P_max, int Hq, int Hkv, int D,
                                         int S_max);
@@ -223,12 +239,30 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len,
  *   packed (dev) [B,P_max,row_len] or NULL; unpacked (dev) [B,W,L,row_len] or NULL
  *   match_len (dev) [B,W]; best_beam, accept_len (dev) [B];
  *   accepted_tokens (dev) [B,L]
+ * An unpacker entry of -1 (a padding candidate of a ragged batch) unpacks
+ * to a zero row.
  */
 int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker,
                      const int32_t *packed_argmax, const void *packed, void *unpacked,
                      int dtype, int64_t row_len, int B, int W, int L,
                      int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
                      int32_t *accepted_tokens, rd_stream_t stream);
+
+/*
+ * Steps 3b + 4 for a ragged batch (beam_width, beam_len as for
+ * rd_pack_beams_mask_ragged).  Only beams w < beam_width[b] and positions
+ * below beam_len[b] take part: n <= beam_len[b]-1, padding beams get
+ * match_len -1, and a request with no beam or no position accepts nothing
+ * (best_beam = accept_len = -1, accepted_tokens all -1, which
+ * rd_commit_accepted leaves unchanged).  Padding candidates unpack to zero
+ * rows.  Otherwise exactly rd_unpack_accept.
+ */
+int rd_unpack_accept_ragged(const int32_t *beams, const int32_t *beam_width,
+                            const int32_t *beam_len, const int32_t *unpacker,
+                            const int32_t *packed_argmax, const void *packed, void *unpacked,
+                            int dtype, int64_t row_len, int B, int W, int L,
+                            int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
+                            int32_t *accepted_tokens, rd_stream_t stream);
 
 /*
  * After step 4 -- commit the accepted path.  [TRT] intro: the best path is

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
-    "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_tree_attention", "rd_tree_attention_paged", "rd_tree_attention_workspace_size",
+    "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_pack_beams_mask_ragged", "rd_tree_attention",
+    "rd_tree_attention_paged", "rd_unpack_accept_ragged", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "verify_step",
     "VerifyBuffers",
 ]
@@ -27,6 +28,7 @@ MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 
 EXPORTED_SYMBOLS = (
     "rd_status_string", "rd_version", "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask",
+    "rd_pack_beams_mask_ragged", "rd_unpack_accept_ragged",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
 )
@@ -62,6 +64,8 @@ def load_library():
         "rd_pack_beams": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "rd_tree_mask": ([vp, vp, i32, i32, i32, vp, vp], i32),
         "rd_pack_beams_mask": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
+        "rd_pack_beams_mask_ragged": ([vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
+        "rd_unpack_accept_ragged": ([vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_tree_attention_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "rd_tree_attention": ([i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                vp, vp, sz, vp], i32),
@@ -163,14 +167,24 @@ def rd_tree_mask(unpacker: torch.Tensor, packed_len: torch.Tensor, *, mask=None)
 
 
 def rd_pack_beams_mask(beams: torch.Tensor, *, packed_tokens=None, packed_len=None, unpacker=None,
-                       packed_depth=None, packed_src=None, mask=None, with_depth_src: bool = True):
-    """Steps 1 + 1b in one launch: returns (pack dict as rd_pack_beams, mask as rd_tree_mask)."""
+                       packed_depth=None, packed_src=None, mask=None, with_depth_src: bool = True,
+                       beam_width=None, beam_len=None):
+    """Steps 1 + 1b in one launch: returns (pack dict as rd_pack_beams, mask as rd_tree_mask).
+
+    With beam_width and beam_len (int32 [B]) the batch is ragged (rd_pack_beams_mask_ragged).
+    """
     lib = load_library()
     _need(beams, "beams", torch.int32)
     if beams.dim() != 3:
         raise ValueError("beams must be [B, W, L]")
     B, W, L = beams.shape
     dev = beams.device
+    ragged = beam_width is not None or beam_len is not None
+    if ragged:
+        if beam_width is None or beam_len is None:
+            raise ValueError("give both beam_width and beam_len")
+        _need(beam_width, "beam_width", torch.int32, (B,), dev)
+        _need(beam_len, "beam_len", torch.int32, (B,), dev)
     P = W * L
     out = {
         "tokens": _out(packed_tokens, "packed_tokens", (B, P), torch.int32, dev),
@@ -180,9 +194,20 @@ def rd_pack_beams_mask(beams: torch.Tensor, *, packed_tokens=None, packed_len=No
         "src": _out(packed_src, "packed_src", (B, P), torch.int32, dev) if with_depth_src else None,
     }
     mask = _out(mask, "mask", (B, P, (P + 31) // 32), torch.int32, dev)
-    _check(lib.rd_pack_beams_mask(_p(beams), B, W, L, _p(out["tokens"]), _p(out["length"]), _p(out["unpacker"]),
-                                  _p(out["depth"]), _p(out["src"]), _p(mask), _stream(beams)), "rd_pack_beams_mask")
+    if ragged:
+        _check(lib.rd_pack_beams_mask_ragged(_p(beams), _p(beam_width), _p(beam_len), B, W, L, _p(out["tokens"]),
+                                             _p(out["length"]), _p(out["unpacker"]), _p(out["depth"]),
+                                             _p(out["src"]), _p(mask), _stream(beams)), "rd_pack_beams_mask_ragged")
+    else:
+        _check(lib.rd_pack_beams_mask(_p(beams), B, W, L, _p(out["tokens"]), _p(out["length"]), _p(out["unpacker"]),
+                                      _p(out["depth"]), _p(out["src"]), _p(mask), _stream(beams)),
+               "rd_pack_beams_mask")
     return out, mask
+
+
+def rd_pack_beams_mask_ragged(beams, beam_width, beam_len, **kw):
+    """Steps 1 + 1b for a ragged batch (see rd_pack_beams_mask)."""
+    return rd_pack_beams_mask(beams, beam_width=beam_width, beam_len=beam_len, **kw)
 
 
 def rd_tree_attention_workspace_size(dtype_code: int, B, P_max, Hq, Hkv, D, S_max) -> int:
@@ -283,12 +308,21 @@ def rd_lm_head_argmax(hidden, packed_len, weight, *, want_logits: bool = True, l
 
 
 def rd_unpack_accept(beams, unpacker, packed_argmax, packed=None, *, unpacked=None, match_len=None,
-                     best_beam=None, accept_len=None, accepted_tokens=None) -> dict:
-    """Steps 3b + 4: optional gather of packed rows to [B,W,L,X] and greedy accept."""
+                     best_beam=None, accept_len=None, accepted_tokens=None, beam_width=None, beam_len=None) -> dict:
+    """Steps 3b + 4: optional gather of packed rows to [B,W,L,X] and greedy accept.
+
+    With beam_width and beam_len (int32 [B]) the batch is ragged (rd_unpack_accept_ragged).
+    """
     lib = load_library()
     _need(beams, "beams", torch.int32)
     B, W, L = beams.shape
     dev = beams.device
+    ragged = beam_width is not None or beam_len is not None
+    if ragged:
+        if beam_width is None or beam_len is None:
+            raise ValueError("give both beam_width and beam_len")
+        _need(beam_width, "beam_width", torch.int32, (B,), dev)
+        _need(beam_len, "beam_len", torch.int32, (B,), dev)
     _need(unpacker, "unpacker", torch.int32, (B, W, L), dev)
     _need(packed_argmax, "packed_argmax", torch.int32, (B, W * L), dev)
     dt, row_len = RD_BF16, 0
@@ -308,10 +342,22 @@ def rd_unpack_accept(beams, unpacker, packed_argmax, packed=None, *, unpacked=No
         "accept_len": _out(accept_len, "accept_len", (B,), torch.int32, dev),
         "accepted_tokens": _out(accepted_tokens, "accepted_tokens", (B, L), torch.int32, dev),
     }
-    _check(lib.rd_unpack_accept(_p(beams), _p(unpacker), _p(packed_argmax), _p(packed), _p(unpacked), dt, row_len,
-                                B, W, L, _p(res["match_len"]), _p(res["best_beam"]), _p(res["accept_len"]),
-                                _p(res["accepted_tokens"]), _stream(beams)), "rd_unpack_accept")
+    if ragged:
+        _check(lib.rd_unpack_accept_ragged(_p(beams), _p(beam_width), _p(beam_len), _p(unpacker), _p(packed_argmax),
+                                           _p(packed), _p(unpacked), dt, row_len, B, W, L, _p(res["match_len"]),
+                                           _p(res["best_beam"]), _p(res["accept_len"]), _p(res["accepted_tokens"]),
+                                           _stream(beams)), "rd_unpack_accept_ragged")
+    else:
+        _check(lib.rd_unpack_accept(_p(beams), _p(unpacker), _p(packed_argmax), _p(packed), _p(unpacked), dt,
+                                    row_len, B, W, L, _p(res["match_len"]), _p(res["best_beam"]),
+                                    _p(res["accept_len"]), _p(res["accepted_tokens"]), _stream(beams)),
+               "rd_unpack_accept")
     return res
+
+
+def rd_unpack_accept_ragged(beams, beam_width, beam_len, unpacker, packed_argmax, packed=None, **kw) -> dict:
+    """Steps 3b + 4 for a ragged batch (see rd_unpack_accept)."""
+    return rd_unpack_accept(beams, unpacker, packed_argmax, packed, beam_width=beam_width, beam_len=beam_len, **kw)
 
 
 def rd_commit_accepted(unpacker, best_beam, accept_len, k_new, v_new, k_cache, v_cache, kv_len, hidden=None, *,
@@ -414,7 +460,7 @@ class VerifyBuffers:
 
 
 def verify_step(beams, q, k_new, v_new, k_cache, v_cache, kv_len, hidden, weight, *, want_logits=True,
-                buffers: VerifyBuffers | None = None, scale: float = 0.0) -> dict:
+                buffers: VerifyBuffers | None = None, scale: float = 0.0, beam_width=None, beam_len=None) -> dict:
     """One verification step: pack+mask, attention, projection, unpack+accept, enqueued in order on the current stream.
 
     q/k_new/v_new/hidden are in packed layout [B, W*L, ...] (rows past the packed length are ignored).
@@ -423,7 +469,8 @@ def verify_step(beams, q, k_new, v_new, k_cache, v_cache, kv_len, hidden, weight
     bufs = buffers
     pk, mask = rd_pack_beams_mask(beams, **({} if bufs is None else {
         "packed_tokens": bufs.pack["tokens"], "packed_len": bufs.pack["length"], "unpacker": bufs.pack["unpacker"],
-        "packed_depth": bufs.pack["depth"], "packed_src": bufs.pack["src"], "mask": bufs.mask}))
+        "packed_depth": bufs.pack["depth"], "packed_src": bufs.pack["src"], "mask": bufs.mask}),
+        beam_width=beam_width, beam_len=beam_len)
     attn = rd_tree_attention(q, k_new, v_new, k_cache, v_cache, kv_len, mask, pk["length"], scale=scale,
                              out=None if bufs is None else bufs.attn,
                              workspace=None if bufs is None else bufs.attn_ws)
@@ -432,5 +479,6 @@ def verify_step(beams, q, k_new, v_new, k_cache, v_cache, kv_len, hidden, weight
                                        argmax=None if bufs is None else bufs.argmax,
                                        workspace=None if bufs is None else bufs.lm_ws)
     acc = rd_unpack_accept(beams, pk["unpacker"], argmax, logits,
-                           **({} if bufs is None else {"unpacked": bufs.unpacked, **bufs.accept}))
+                           **({} if bufs is None else {"unpacked": bufs.unpacked, **bufs.accept}),
+                           beam_width=beam_width, beam_len=beam_len)
     return {"pack": pk, "mask": mask, "attn": attn, "logits": logits, "argmax": argmax, **acc}

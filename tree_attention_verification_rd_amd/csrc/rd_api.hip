@@ -68,8 +68,19 @@ int rd_pack_beams_mask(const int32_t *beams, int B, int W, int L, int32_t *packe
     if (B == 0 || W == 0 || L == 0) return RD_OK;
     if (!beams || !packed_tokens || !packed_len || !unpacker || !mask) return RD_E_ARG;
     if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
-    return hip_status(rd::launch_pack_mask(beams, B, W, L, packed_tokens, packed_len, unpacker, packed_depth,
-                                           packed_src, mask, as_stream(stream)));
+    return hip_status(rd::launch_pack_mask(beams, nullptr, nullptr, B, W, L, packed_tokens, packed_len, unpacker,
+                                           packed_depth, packed_src, mask, as_stream(stream)));
+}
+
+int rd_pack_beams_mask_ragged(const int32_t *beams, const int32_t *beam_width, const int32_t *beam_len, int B, int W,
+                              int L, int32_t *packed_tokens, int32_t *packed_len, int32_t *unpacker,
+                              int32_t *packed_depth, int32_t *packed_src, uint32_t *mask, rd_stream_t stream) {
+    if (!beam_shape_ok(B, W, L)) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!beams || !beam_width || !beam_len || !packed_tokens || !packed_len || !unpacker || !mask) return RD_E_ARG;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    return hip_status(rd::launch_pack_mask(beams, beam_width, beam_len, B, W, L, packed_tokens, packed_len, unpacker,
+                                           packed_depth, packed_src, mask, as_stream(stream)));
 }
 
 int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int W, int L, uint32_t *mask,
@@ -171,9 +182,14 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, 
                                          ws, as_stream(stream)));
 }
 
-int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *packed_argmax, const void *packed,
-                     void *unpacked, int dtype, int64_t row_len, int B, int W, int L, int32_t *match_len,
-                     int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens, rd_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int unpack_accept(const int32_t *beams, const int32_t *bwid, const int32_t *blen, const int32_t *unpacker,
+                  const int32_t *packed_argmax, const void *packed, void *unpacked, int dtype, int64_t row_len, int B,
+                  int W, int L, int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
+                  int32_t *accepted_tokens, rd_stream_t stream) {
     if (!beam_shape_ok(B, W, L) || row_len < 0) return RD_E_ARG;
     if (B == 0 || W == 0 || L == 0) return RD_OK;
     if (!beams || !unpacker || !packed_argmax || !match_len || !best_beam || !accept_len || !accepted_tokens)
@@ -190,7 +206,27 @@ int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_
     }
     return hip_status(rd::launch_unpack_accept(row_bytes ? packed : nullptr, row_bytes ? unpacked : nullptr, unpacker,
                                                row_bytes, beams, packed_argmax, B, W, L, match_len, best_beam,
-                                               accept_len, accepted_tokens, s));
+                                               accept_len, accepted_tokens, s, bwid, blen));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rd_unpack_accept(const int32_t *beams, const int32_t *unpacker, const int32_t *packed_argmax, const void *packed,
+                     void *unpacked, int dtype, int64_t row_len, int B, int W, int L, int32_t *match_len,
+                     int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens, rd_stream_t stream) {
+    return unpack_accept(beams, nullptr, nullptr, unpacker, packed_argmax, packed, unpacked, dtype, row_len, B, W, L,
+                         match_len, best_beam, accept_len, accepted_tokens, stream);
+}
+
+int rd_unpack_accept_ragged(const int32_t *beams, const int32_t *beam_width, const int32_t *beam_len,
+                            const int32_t *unpacker, const int32_t *packed_argmax, const void *packed, void *unpacked,
+                            int dtype, int64_t row_len, int B, int W, int L, int32_t *match_len, int32_t *best_beam,
+                            int32_t *accept_len, int32_t *accepted_tokens, rd_stream_t stream) {
+    if (B > 0 && W > 0 && L > 0 && (!beam_width || !beam_len)) return RD_E_ARG;
+    return unpack_accept(beams, beam_width, beam_len, unpacker, packed_argmax, packed, unpacked, dtype, row_len, B, W,
+                         L, match_len, best_beam, accept_len, accepted_tokens, stream);
 }
 
 int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,

@@ -13,8 +13,10 @@ constexpr int kMaxBeamLen = 16;
 hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t *tokens,
                              int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
                              hipStream_t stream);
-hipError_t launch_pack_mask(const int32_t *beams, int B, int W, int L, int32_t *tokens, int32_t *plen,
-                            int32_t *unpacker, int32_t *depth, int32_t *src, uint32_t *mask, hipStream_t stream);
+// bwid / blen: per-request beam count and length of a ragged batch, or null (full W, L)
+hipError_t launch_pack_mask(const int32_t *beams, const int32_t *bwid, const int32_t *blen, int B, int W, int L,
+                            int32_t *tokens, int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
+                            uint32_t *mask, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t *unpacker, const int32_t *plen, int B, int W, int L,
                             uint32_t *mask, hipStream_t stream);
 
@@ -61,7 +63,8 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
 hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,
                                 const int32_t *beams, const int32_t *pargmax, int B, int W, int L,
                                 int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
-                                int32_t *accepted, hipStream_t stream);
+                                int32_t *accepted, hipStream_t stream, const int32_t *bwid = nullptr,
+                                const int32_t *blen = nullptr);
 
 // commit of the accepted path (esize = bytes per element)
 hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,

@@ -24,9 +24,11 @@ namespace rd {
 // Packs request b with one wavefront and no workgroup barrier, so it can
 // run in the first wavefront of a larger workgroup.  sb and sf are LDS
 // scratch of W*L ints (the beams, the node names); when su (LDS) is given
-// the unpacker rows are also left there for the fused mask.  Returns the
-// packed length (in every lane).
-__device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, int b, int W, int L,
+// the unpacker rows are also left there for the fused mask.  A ragged
+// request uses only its first Wb beams and Lb positions (inflight batching
+// mixes requests of different shapes); its padding candidates open no node
+// and get unpacker -1.  Returns the packed length (in every lane).
+__device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, int b, int W, int L, int Wb, int Lb,
                                             int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
                                             int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
                                             int32_t *__restrict__ src, int32_t *sb, int32_t *sf, int32_t *su) {
@@ -38,25 +40,26 @@ __device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, i
     // in order, so completing its own writes is enough
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    const bool active = lane < W;
+    const bool active = lane < W;  // writes an unpacker row
+    const bool real = lane < Wb;   // a beam of the request
     const int own0 = active ? lane * L : 0;
     int fprev = 0;  // every beam hangs off the same virtual root
     int m = 0;
-    for (int l = 0; l < L; ++l) {  // uniform
+    for (int l = 0; l < Lb; ++l) {  // uniform
         const int tok = sb[own0 + l];
         int f = lane;
-        for (int v = 0; v < W; ++v) {  // uniform
+        for (int v = 0; v < Wb; ++v) {  // uniform
             const int pv = __builtin_amdgcn_readlane(fprev, v);
             const int tv = __builtin_amdgcn_readlane(tok, v);
             f = (v < f && pv == fprev && tv == tok) ? v : f;
         }
-        if (active) sf[own0 + l] = f;
+        if (real) sf[own0 + l] = f;
         m += (f < lane) ? 1 : 0;
         fprev = f;
     }
 
     // exclusive prefix sum of new-slot counts over lanes, bit plane by bit plane
-    const int cnt = active ? (L - m) : 0;  // 0..16: five bits
+    const int cnt = real ? (Lb - m) : 0;  // 0..16: five bits
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     int base = 0, total = 0;
 #pragma unroll
@@ -70,12 +73,13 @@ __device__ __forceinline__ int pack_request(const int32_t *__restrict__ beams, i
     int32_t *urow = unpacker + static_cast<size_t>(b) * P + own0;
     const size_t row = static_cast<size_t>(b) * P;
     for (int l = 0; l < L; ++l) {  // uniform: every lane takes part in the shuffles
-        const int o = sf[own0 + l];
-        const int slot = __shfl(base, o, kWave) + l - __shfl(m, o, kWave);
+        const bool cand = real && l < Lb;
+        const int o = cand ? sf[own0 + l] : 0;
+        const int slot = cand ? __shfl(base, o, kWave) + l - __shfl(m, o, kWave) : -1;
         if (active) {
             urow[l] = slot;
             if (su) su[own0 + l] = slot;
-            if (l >= m) {  // a node this beam opens
+            if (cand && l >= m) {  // a node this beam opens
                 tokens[row + slot] = sb[own0 + l];
                 if (depth) depth[row + slot] = l;
                 if (src) src[row + slot] = own0 + l;
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(64) void k_pack_beams(const int32_t *__restrict__ b
                                                    int32_t *__restrict__ src) {
     __shared__ int32_t sb[kMaxBeams * kMaxBeamLen];
     __shared__ int32_t sf[kMaxBeams * kMaxBeamLen];
-    pack_request(beams, blockIdx.x, W, L, tokens, plen, unpacker, depth, src, sb, sf, nullptr);
+    pack_request(beams, blockIdx.x, W, L, W, L, tokens, plen, unpacker, depth, src, sb, sf, nullptr);
 }
 
 // Step 1b.  [SURV] SpecInfer "Token Tree Verifier": bit q of row p is set iff
@@ -148,7 +152,10 @@ __global__ __launch_bounds__(256) void k_tree_mask(const int32_t *__restrict__ u
 
 // Steps 1 and 1b in one launch: the first wavefront packs the request and
 // leaves its unpacker in LDS, then the workgroup builds the mask from it.
+// bwid / blen (either may be null: all W beams, all L positions) give a
+// ragged request's beam count and length.
 __global__ __launch_bounds__(256) void k_pack_mask(const int32_t *__restrict__ beams, int W, int L,
+                                                   const int32_t *__restrict__ bwid, const int32_t *__restrict__ blen,
                                                    int32_t *__restrict__ tokens, int32_t *__restrict__ plen,
                                                    int32_t *__restrict__ unpacker, int32_t *__restrict__ depth,
                                                    int32_t *__restrict__ src, uint32_t *__restrict__ mask) {
@@ -158,8 +165,10 @@ __global__ __launch_bounds__(256) void k_pack_mask(const int32_t *__restrict__ b
     __shared__ int32_t parent[kMaxBeams * kMaxBeamLen];
     __shared__ int32_t n_sh;
     const int b = blockIdx.x;
+    const int Wb = bwid ? min(max(__builtin_amdgcn_readfirstlane(bwid[b]), 0), W) : W;
+    const int Lb = blen ? min(max(__builtin_amdgcn_readfirstlane(blen[b]), 0), L) : L;
     if (threadIdx.x < kWave) {  // wave-uniform branch; the pack has no workgroup barrier
-        const int n = pack_request(beams, b, W, L, tokens, plen, unpacker, depth, src, sb, sf, su);
+        const int n = pack_request(beams, b, W, L, Wb, Lb, tokens, plen, unpacker, depth, src, sb, sf, su);
         if (threadIdx.x == 0) n_sh = n;
     }
     __syncthreads();
@@ -174,10 +183,11 @@ hipError_t launch_pack_beams(const int32_t *beams, int B, int W, int L, int32_t 
     return hipGetLastError();
 }
 
-hipError_t launch_pack_mask(const int32_t *beams, int B, int W, int L, int32_t *tokens, int32_t *plen,
-                            int32_t *unpacker, int32_t *depth, int32_t *src, uint32_t *mask, hipStream_t stream) {
-    hipLaunchKernelGGL(k_pack_mask, dim3(B), dim3(256), 0, stream, beams, W, L, tokens, plen, unpacker, depth, src,
-                       mask);
+hipError_t launch_pack_mask(const int32_t *beams, const int32_t *bwid, const int32_t *blen, int B, int W, int L,
+                            int32_t *tokens, int32_t *plen, int32_t *unpacker, int32_t *depth, int32_t *src,
+                            uint32_t *mask, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pack_mask, dim3(B), dim3(256), 0, stream, beams, W, L, bwid, blen, tokens, plen, unpacker,
+                       depth, src, mask);
     return hipGetLastError();
 }
 

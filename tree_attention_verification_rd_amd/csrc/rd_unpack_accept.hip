@@ -9,11 +9,14 @@ namespace rd {
 // Greedy accept: one wavefront per request, one lane per beam.  Lane w walks
 // its beam while the draft at j+1 equals the target's choice at j; the best
 // beam is the max of the key (match length, -w) across lanes, so ties go to
-// the lowest beam.
+// the lowest beam.  A ragged request (bwid / blen given) uses only its first
+// Wb beams and Lb positions; padding beams report match length -1, and a
+// request with no beam or no position accepts nothing (-1 everywhere).
 struct AcceptArgs {
     const int32_t *beams, *unpacker, *pargmax;
     int W, L;
     int32_t *match_len, *best_beam, *accept_len, *accepted;
+    const int32_t *bwid, *blen;
 };
 
 __device__ __forceinline__ void accept_request(const AcceptArgs &a, int b, int lane) {
@@ -24,24 +27,29 @@ __device__ __forceinline__ void accept_request(const AcceptArgs &a, int b, int l
         const int slot = a.unpacker[(static_cast<size_t>(b) * W + w) * L + l];
         return am[min(max(slot, 0), P - 1)];
     };
+    const int Wb = a.bwid ? min(max(a.bwid[b], 0), W) : W;
+    const int Lb = a.blen ? min(max(a.blen[b], 0), L) : L;
+    const bool real = lane < Wb && Lb > 0;
     int n = 0;
-    if (lane < W) {
+    if (real) {
         const int32_t *bw = a.beams + (static_cast<size_t>(b) * W + lane) * L;
-        while (n < L - 1 && bw[n + 1] == target_at(lane, n)) ++n;
-        a.match_len[static_cast<size_t>(b) * W + lane] = n;
+        while (n < Lb - 1 && bw[n + 1] == target_at(lane, n)) ++n;
     }
-    int key = (lane < W) ? ((n << 6) | (63 - lane)) : -1;
+    if (lane < W) a.match_len[static_cast<size_t>(b) * W + lane] = real ? n : -1;
+    int key = real ? ((n << 6) | (63 - lane)) : -1;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) key = max(key, shfl_xor(key, off));
-    const int best = 63 - (key & 63);
-    const int nbest = key >> 6;
+    const int best = key < 0 ? -1 : 63 - (key & 63);
+    const int nbest = key < 0 ? -1 : key >> 6;
     if (lane == 0) {
         a.best_beam[b] = best;
         a.accept_len[b] = nbest;
     }
     if (lane < L) {
         int t = -1;
-        if (lane < nbest)
+        if (best < 0)
+            t = -1;
+        else if (lane < nbest)
             t = a.beams[(static_cast<size_t>(b) * W + best) * L + lane + 1];
         else if (lane == nbest)
             t = target_at(best, nbest);
@@ -69,7 +77,8 @@ __global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ pac
     const int64_t row = blk / nchunks;
     const int chunk = static_cast<int>(blk % nchunks);
     const int64_t b = row / WL;
-    const int slot = min(max(unpacker[row], 0), P - 1);
+    const int uslot = unpacker[row];  // -1: a padding candidate of a ragged request, unpacked as zeros
+    const int slot = min(max(uslot, 0), P - 1);
     const T *s = packed + (b * P + slot) * row_elems;
     T *d = out + row * row_elems;
     const int64_t base = static_cast<int64_t>(chunk) * (256 * UNROLL) + threadIdx.x;
@@ -77,7 +86,7 @@ __global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ pac
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int64_t i = base + u * 256;
-        if (i < row_elems) v[u] = s[i];
+        if (i < row_elems) v[u] = (uslot >= 0) ? s[i] : T{};
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -89,8 +98,8 @@ __global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ pac
 hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,
                                 const int32_t *beams, const int32_t *pargmax, int B, int W, int L,
                                 int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
-                                int32_t *accepted, hipStream_t stream) {
-    AcceptArgs acc{beams, unpacker, pargmax, W, L, match_len, best_beam, accept_len, accepted};
+                                int32_t *accepted, hipStream_t stream, const int32_t *bwid, const int32_t *blen) {
+    AcceptArgs acc{beams, unpacker, pargmax, W, L, match_len, best_beam, accept_len, accepted, bwid, blen};
     if (!packed || !unpacked || row_bytes <= 0) {
         hipLaunchKernelGGL(k_accept, dim3(B), dim3(kWave), 0, stream, acc);
         return hipGetLastError();
