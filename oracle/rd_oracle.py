@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "pack_beams", "tree_mask", "mask_to_bits", "attention_per_beam",
     "attention_packed", "gather_pages", "attention_paged", "lm_head_logits", "argmax_first", "unpack",
-    "greedy_accept", "commit_accepted", "commit_accepted_paged", "verify_requests",
+    "greedy_accept", "stochastic_accept", "commit_accepted", "commit_accepted_paged", "verify_requests",
 ]
 
 
@@ -332,6 +332,85 @@ def greedy_accept(beams: np.ndarray, target: np.ndarray, beam_width=None, beam_l
         accepted[b, :len(toks)] = toks
     return {"match_len": match_len, "best_beam": best_beam, "accept_len": accept_len,
             "accepted_tokens": accepted}
+
+
+def _children(unpacker_b: np.ndarray, n: int) -> list:
+    """Children of every slot of one request's tree, in increasing slot order."""
+    W, L = unpacker_b.shape
+    kids = [set() for _ in range(n)]
+    for w in range(W):
+        for l in range(L - 1):
+            s, c = int(unpacker_b[w, l]), int(unpacker_b[w, l + 1])
+            if 0 <= s < n and 0 <= c < n:
+                kids[s].add(c)
+    return [sorted(k) for k in kids]
+
+
+def stochastic_accept(beams, unpacker, packed_len, packed_tokens, logits, q, u_accept, u_bonus) -> dict:
+    """Stochastic verification of the token tree by multi-step speculative sampling.
+
+    [SURV] "rejection sampling": with proposal q and target p, a sample x
+    drawn from q and kept when u < p(x)/q(x), u ~ U(0,1), is distributed as
+    p.  [SURV] SpecInfer: random decoding verifies the tree by multi-step
+    speculative sampling -- each drafted candidate in turn gets that test;
+    when every candidate is rejected, the sample comes from what is left of
+    p -- and the result has the target's sampling distribution.
+
+    Readings (the pages give the rule, not the tree walk): the walk starts at
+    slot 0, the depth-0 node of beam 0 (the shared initial token).  At node
+    u, p = softmax(logits[b, u]) and q = q[b, u] (the drafter's distribution
+    for the token after u).  Children of u are tried in increasing slot
+    order; the i-th child tried at depth d, token x, is accepted when
+    u_accept[b, d, i] * q(x) < p(x), and the walk moves to it.  A rejection
+    replaces p by max(p - q, 0) / sum(max(p - q, 0)) (q unchanged; if that
+    sum is 0, p stays).  When no child is accepted, or u is a leaf, the bonus
+    token is the smallest k with cumsum(p)[k] > u_bonus[b] * sum(p).
+
+    logits, q [B,P,V]; u_accept [B,L,W]; u_bonus [B].  Returns int32:
+    accept_len [B] (accepted drafts n), best_beam [B] (lowest beam whose
+    depth-n node is the last accepted one), accepted_tokens [B,L] (the n
+    drafts then the bonus, pad -1), path [B,L] (slots from depth 0, pad -1).
+    """
+    B, W, L = unpacker.shape
+    accept_len = np.full(B, -1, np.int32)
+    best_beam = np.full(B, -1, np.int32)
+    accepted = np.full((B, L), -1, np.int32)
+    path = np.full((B, L), -1, np.int32)
+    for b in range(B):
+        n_slots = int(packed_len[b])
+        if n_slots == 0:
+            continue
+        kids = _children(unpacker[b], n_slots)
+        u, d, toks = 0, 0, []
+        path[b, 0] = 0
+        while True:
+            lg = np.asarray(logits[b, u], np.float64)
+            e = np.exp(lg - lg.max())
+            p = e / e.sum()
+            qq = np.asarray(q[b, u], np.float64)
+            moved = False
+            for i, c in enumerate(kids[u]):
+                x = int(packed_tokens[b, c])
+                if u_accept[b, d, i] * qq[x] < p[x]:
+                    u, d = c, d + 1
+                    toks.append(x)
+                    path[b, d] = c
+                    moved = True
+                    break
+                res = np.maximum(p - qq, 0.0)
+                z = res.sum()
+                if z > 0:
+                    p = res / z
+            if not moved:
+                break
+        cdf = np.cumsum(p)
+        bonus = int(np.searchsorted(cdf, u_bonus[b] * cdf[-1], side="right"))
+        bonus = min(bonus, len(p) - 1)
+        n = len(toks)
+        accept_len[b] = n
+        best_beam[b] = next(w for w in range(W) if unpacker[b, w, n] == u)
+        accepted[b, :n + 1] = toks + [bonus]
+    return {"accept_len": accept_len, "best_beam": best_beam, "accepted_tokens": accepted, "path": path}
 
 
 # ------------------------------------------------------- after step 4 --
