@@ -325,6 +325,24 @@ def main():
         rd.rd_unpack_accept(beams, r_pk["unpacker"], bufs.argmax, bufs.logits if full else None,
                             unpacked=bufs.unpacked, beam_width=r_bw, beam_len=r_bl, **r_acc)
 
+    # Stochastic step 4 on the step's own logits (full variant), with a
+    # seeded draft distribution and uniforms.
+    stoch_us = None
+    if full:
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(seed + 23)
+        s_q = torch.softmax(torch.randn((B, P, cfg.V), generator=gq, device=dev), dim=-1)
+        s_ua = torch.rand((B, cfg.L, cfg.W), generator=gq, device=dev)
+        s_ub = torch.rand((B,), generator=gq, device=dev)
+        s_out = {k: torch.empty_like(v) for k, v in bufs.accept.items() if k != "match_len"}
+        s_path = torch.empty_like(bufs.accept["accepted_tokens"])
+
+        def stoch_call(i):
+            rd.rd_stochastic_accept(pk["unpacker"], pk["length"], pk["tokens"], bufs.logits, s_q, s_ua, s_ub,
+                                    path=s_path, **s_out)
+
+        stoch_us = queued_call_us(stoch_call, lambda: None)
+
     ragged_pack_us = queued_call_us(ragged_pack_call, lambda: None)
     ragged_accept_us = queued_call_us(ragged_accept_call, lambda: None)
     ragged_packed = int(r_pk["length"].sum().item())
@@ -377,6 +395,7 @@ def main():
         "gpu_ms_per_step": round(ms_gpu, 4),
         "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
                        "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
+        "stochastic": {"call": "rd_stochastic_accept", "avg_us": None if stoch_us is None else round(stoch_us, 2)},
         "ragged": {"calls": "rd_pack_beams_mask_ragged + rd_unpack_accept_ragged",
                    "candidates": int((r_bw * r_bl).sum().item()), "packed_tokens": ragged_packed,
                    "pack_mask_us": round(ragged_pack_us, 2), "unpack_accept_us": round(ragged_accept_us, 2)},

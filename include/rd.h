@@ -265,6 +265,39 @@ int rd_unpack_accept_ragged(const int32_t *beams, const int32_t *beam_width,
                             int32_t *accepted_tokens, rd_stream_t stream);
 
 /*
+ * Step 4, stochastic variant: multi-step speculative sampling over the
+ * token tree.  [SURV] rejection sampling: a draft x ~ q kept when
+ * u < p(x)/q(x) is distributed as p; [SURV] SpecInfer: random decoding
+ * tests each drafted candidate in turn and, when all are rejected, samples
+ * what remains of p, matching the target's sampling distribution.
+ * Walk from slot 0 (beam 0's depth-0 node).  At node u, p = softmax of
+ * logits[b,u,:] (fp32) and q = q[b,u,:] (the drafter's distribution for the
+ * next token).  Children of u are tried in increasing slot order; the i-th
+ * tried at depth d, token x = packed_tokens[b,child], is accepted when
+ * u_accept[b,d,i] * q(x) < p(x), and the walk moves to it; a rejection
+ * replaces p by max(p - q, 0) / sum (p kept if the sum is 0).  When no child
+ * is accepted or u is a leaf, the bonus token is the first index whose
+ * running sum of p exceeds u_bonus[b] times its total.
+ *
+ *   unpacker, packed_len, packed_tokens (dev) from rd_pack_beams*
+ *   logits (dev) [B,P_max,V] in dtype (e.g. rd_lm_head_argmax's output)
+ *   q (dev) fp32 [B,P_max,V]; u_accept (dev) fp32 [B,L,W]; u_bonus (dev) fp32 [B]
+ *   best_beam, accept_len (dev) [B]: the lowest beam holding the last
+ *     accepted node and the number n of accepted drafts (-1 for an empty
+ *     request), as rd_unpack_accept reports them for rd_commit_accepted
+ *   accepted_tokens (dev) [B,L]: n drafts, then the bonus, then -1
+ *   path (dev) [B,L] or NULL: slots of the walk from depth 0, then -1
+ * One workgroup per request, no workspace; deterministic.  Errors: RD_E_ARG
+ * for null required pointers or negative sizes, RD_E_UNSUPPORTED for
+ * W > 64, L > 16 or an unknown dtype.
+ */
+int rd_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *packed_len,
+                         const int32_t *packed_tokens, const void *logits, const float *q,
+                         const float *u_accept, const float *u_bonus, int B, int W, int L, int V,
+                         int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens,
+                         int32_t *path, rd_stream_t stream);
+
+/*
  * After step 4 -- commit the accepted path.  [TRT] intro: the best path is
  * accepted before the next drafting round, so its tokens join the context;
  * [NEWS] "RNN draft model": the drafter continues from the target's latest

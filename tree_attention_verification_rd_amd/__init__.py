@@ -18,7 +18,8 @@ __all__ = [
     "RD_OK", "RD_F32", "RD_BF16", "RdError", "lib_path", "load_library", "EXPORTED_SYMBOLS",
     "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_pack_beams_mask_ragged", "rd_tree_attention",
     "rd_tree_attention_paged", "rd_unpack_accept_ragged", "rd_tree_attention_workspace_size",
-    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "verify_step",
+    "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "rd_stochastic_accept",
+    "verify_step",
     "VerifyBuffers",
 ]
 
@@ -31,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "rd_pack_beams_mask_ragged", "rd_unpack_accept_ragged",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
+    "rd_stochastic_accept",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +78,7 @@ def load_library():
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_commit_accepted": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                 vp], i32),
+        "rd_stochastic_accept": ([i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_commit_accepted_paged": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64, i32,
                                       vp, i32, vp, vp, vp], i32),
     }
@@ -436,6 +439,37 @@ def rd_commit_accepted_paged(unpacker, best_beam, accept_len, k_new, v_new, k_pa
                                         k_pages.shape[2], _p(block_table), block_table.shape[1], _p(kv_len),
                                         _p(hidden_next), _stream(unpacker)), "rd_commit_accepted_paged")
     return hidden_next
+
+
+def rd_stochastic_accept(unpacker, packed_len, packed_tokens, logits, q, u_accept, u_bonus, *, best_beam=None,
+                         accept_len=None, accepted_tokens=None, path=None) -> dict:
+    """Stochastic step 4 (multi-step speculative sampling over the tree); see include/rd.h."""
+    lib = load_library()
+    _need(unpacker, "unpacker", torch.int32)
+    B, W, L = unpacker.shape
+    dev = unpacker.device
+    P = W * L
+    dt = _dtype_code(logits)
+    _need(logits, "logits", logits.dtype, None, dev)
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (B, P):
+        raise ValueError("logits must be [B, W*L, V]")
+    V = logits.shape[2]
+    _need(packed_len, "packed_len", torch.int32, (B,), dev)
+    _need(packed_tokens, "packed_tokens", torch.int32, (B, P), dev)
+    _need(q, "q", torch.float32, (B, P, V), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, L, W), dev)
+    _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
+    res = {
+        "best_beam": _out(best_beam, "best_beam", (B,), torch.int32, dev),
+        "accept_len": _out(accept_len, "accept_len", (B,), torch.int32, dev),
+        "accepted_tokens": _out(accepted_tokens, "accepted_tokens", (B, L), torch.int32, dev),
+        "path": _out(path, "path", (B, L), torch.int32, dev),
+    }
+    _check(lib.rd_stochastic_accept(dt, _p(unpacker), _p(packed_len), _p(packed_tokens), _p(logits), _p(q),
+                                    _p(u_accept), _p(u_bonus), B, W, L, V, _p(res["best_beam"]),
+                                    _p(res["accept_len"]), _p(res["accepted_tokens"]), _p(res["path"]),
+                                    _stream(unpacker)), "rd_stochastic_accept")
+    return res
 
 
 class VerifyBuffers:
