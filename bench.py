@@ -334,12 +334,14 @@ def main():
         s_q = torch.softmax(torch.randn((B, P, cfg.V), generator=gq, device=dev), dim=-1)
         s_ua = torch.rand((B, cfg.L, cfg.W), generator=gq, device=dev)
         s_ub = torch.rand((B,), generator=gq, device=dev)
+        s_ws = torch.empty(max(rd.rd_stochastic_accept_workspace_size(B, cfg.W, cfg.L), 1), dtype=torch.uint8,
+                           device=dev)
         s_out = {k: torch.empty_like(v) for k, v in bufs.accept.items() if k != "match_len"}
         s_path = torch.empty_like(bufs.accept["accepted_tokens"])
 
         def stoch_call(i):
             rd.rd_stochastic_accept(pk["unpacker"], pk["length"], pk["tokens"], bufs.logits, s_q, s_ua, s_ub,
-                                    path=s_path, **s_out)
+                                    path=s_path, workspace=s_ws, **s_out)
 
         stoch_us = queued_call_us(stoch_call, lambda: None)
 

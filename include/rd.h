@@ -287,15 +287,21 @@ int rd_unpack_accept_ragged(const int32_t *beams, const int32_t *beam_width,
  *     request), as rd_unpack_accept reports them for rd_commit_accepted
  *   accepted_tokens (dev) [B,L]: n drafts, then the bonus, then -1
  *   path (dev) [B,L] or NULL: slots of the walk from depth 0, then -1
- * One workgroup per request, no workspace; deterministic.  Errors: RD_E_ARG
- * for null required pointers or negative sizes, RD_E_UNSUPPORTED for
- * W > 64, L > 16 or an unknown dtype.
+ *   ws (dev) workspace >= rd_stochastic_accept_workspace_size(B, W, L)
+ *           (12 bytes a slot): per slot, the two values of its own test at
+ *           its parent and the bonus token it yields if all its children
+ *           are rejected
+ * Two launches (every slot's statistics, then one walk per request);
+ * deterministic.  Errors: RD_E_ARG for null required pointers or negative
+ * sizes, RD_E_UNSUPPORTED for W > 64, L > 16 or an unknown dtype,
+ * RD_E_WORKSPACE for a small workspace.
  */
+size_t rd_stochastic_accept_workspace_size(int B, int W, int L);
 int rd_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *packed_len,
                          const int32_t *packed_tokens, const void *logits, const float *q,
                          const float *u_accept, const float *u_bonus, int B, int W, int L, int V,
                          int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens,
-                         int32_t *path, rd_stream_t stream);
+                         int32_t *path, void *ws, size_t ws_bytes, rd_stream_t stream);
 
 /*
  * After step 4 -- commit the accepted path.  [TRT] intro: the best path is

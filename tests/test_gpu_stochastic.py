@@ -65,6 +65,7 @@ CASES = {
     "f32": (5, 3, 5, 300, "f32", 1.5, 0.5),
     "llama_vocab": (8, 8, 5, 32000, "bf16", 3.0, 0.9),
     "wide": (3, 64, 8, 1000, "bf16", 2.5, 0.8),
+    "big_vocab": (2, 3, 4, 40000, "bf16", 2.5, 0.8),   # beyond the register-resident row size: streamed passes
 }
 
 

@@ -80,12 +80,14 @@ def test_host_side_validation_without_device():
                                        1 << 20, null) == -1
     assert lib.rd_tree_attention_paged(1, *pa, 8, 64, fake, 4, fake, fake, fake, 0, 8, 4, 4, 128, 0.0, fake, fake,
                                        0, null) == 0
-    # stochastic accept: unknown dtype, null q, empty batch
+    # stochastic accept: unknown dtype, null q, small workspace, empty batch
     st = [fake] * 7  # unpacker, packed_len, packed_tokens, logits, q, u_accept, u_bonus
-    assert lib.rd_stochastic_accept(5, *st, 2, 8, 5, 1000, fake, fake, fake, null, null) == -2
+    assert lib.rd_stochastic_accept(5, *st, 2, 8, 5, 1000, fake, fake, fake, null, fake, 1 << 20, null) == -2
     st_noq = [fake, fake, fake, fake, null, fake, fake]
-    assert lib.rd_stochastic_accept(1, *st_noq, 2, 8, 5, 1000, fake, fake, fake, null, null) == -1
-    assert lib.rd_stochastic_accept(1, *st, 0, 8, 5, 1000, fake, fake, fake, null, null) == 0
+    assert lib.rd_stochastic_accept(1, *st_noq, 2, 8, 5, 1000, fake, fake, fake, null, fake, 1 << 20, null) == -1
+    assert lib.rd_stochastic_accept(1, *st, 2, 8, 5, 1000, fake, fake, fake, null, fake, 16, null) == -3
+    assert lib.rd_stochastic_accept(1, *st, 0, 8, 5, 1000, fake, fake, fake, null, null, 0, null) == 0
+    assert lib.rd_stochastic_accept_workspace_size(2, 8, 5) == 2 * 40 * (8 + 4)   # per slot: test pair, bonus
     # projection: K not a multiple of 8 in bf16, unknown dtype, empty
     assert lib.rd_lm_head_argmax(1, fake, fake, fake, 2, 8, 100, 50, fake, fake, fake, 1 << 20, null) == -2
     assert lib.rd_lm_head_argmax(5, fake, fake, fake, 2, 8, 128, 50, fake, fake, fake, 1 << 20, null) == -2

@@ -19,7 +19,7 @@ __all__ = [
     "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_pack_beams_mask_ragged", "rd_tree_attention",
     "rd_tree_attention_paged", "rd_unpack_accept_ragged", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "rd_stochastic_accept",
-    "verify_step",
+    "rd_stochastic_accept_workspace_size", "verify_step",
     "VerifyBuffers",
 ]
 
@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "rd_pack_beams_mask_ragged", "rd_unpack_accept_ragged",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
-    "rd_stochastic_accept",
+    "rd_stochastic_accept_workspace_size", "rd_stochastic_accept",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,7 +78,8 @@ def load_library():
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_commit_accepted": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                 vp], i32),
-        "rd_stochastic_accept": ([i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
+        "rd_stochastic_accept_workspace_size": ([i32, i32, i32], sz),
+        "rd_stochastic_accept": ([i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
         "rd_commit_accepted_paged": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64, i32,
                                       vp, i32, vp, vp, vp], i32),
     }
@@ -441,8 +442,12 @@ def rd_commit_accepted_paged(unpacker, best_beam, accept_len, k_new, v_new, k_pa
     return hidden_next
 
 
+def rd_stochastic_accept_workspace_size(B, W, L) -> int:
+    return int(load_library().rd_stochastic_accept_workspace_size(B, W, L))
+
+
 def rd_stochastic_accept(unpacker, packed_len, packed_tokens, logits, q, u_accept, u_bonus, *, best_beam=None,
-                         accept_len=None, accepted_tokens=None, path=None) -> dict:
+                         accept_len=None, accepted_tokens=None, path=None, workspace=None) -> dict:
     """Stochastic step 4 (multi-step speculative sampling over the tree); see include/rd.h."""
     lib = load_library()
     _need(unpacker, "unpacker", torch.int32)
@@ -465,10 +470,14 @@ def rd_stochastic_accept(unpacker, packed_len, packed_tokens, logits, q, u_accep
         "accepted_tokens": _out(accepted_tokens, "accepted_tokens", (B, L), torch.int32, dev),
         "path": _out(path, "path", (B, L), torch.int32, dev),
     }
+    need = rd_stochastic_accept_workspace_size(B, W, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
     _check(lib.rd_stochastic_accept(dt, _p(unpacker), _p(packed_len), _p(packed_tokens), _p(logits), _p(q),
                                     _p(u_accept), _p(u_bonus), B, W, L, V, _p(res["best_beam"]),
                                     _p(res["accept_len"]), _p(res["accepted_tokens"]), _p(res["path"]),
-                                    _stream(unpacker)), "rd_stochastic_accept")
+                                    _p(workspace), workspace.numel(), _stream(unpacker)), "rd_stochastic_accept")
     return res
 
 

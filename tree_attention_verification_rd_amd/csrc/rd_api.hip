@@ -229,10 +229,15 @@ int rd_unpack_accept_ragged(const int32_t *beams, const int32_t *beam_width, con
                          L, match_len, best_beam, accept_len, accepted_tokens, stream);
 }
 
+size_t rd_stochastic_accept_workspace_size(int B, int W, int L) {
+    if (!beam_shape_ok(B, W, L) || !beam_shape_supported(W, L)) return 0;
+    return rd::stochastic_workspace_bytes(B, W, L);
+}
+
 int rd_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *packed_len, const int32_t *packed_tokens,
                          const void *logits, const float *q, const float *u_accept, const float *u_bonus, int B,
                          int W, int L, int V, int32_t *best_beam, int32_t *accept_len, int32_t *accepted_tokens,
-                         int32_t *path, rd_stream_t stream) {
+                         int32_t *path, void *ws, size_t ws_bytes, rd_stream_t stream) {
     if (!beam_shape_ok(B, W, L) || V < 0) return RD_E_ARG;
     if (B == 0 || W == 0 || L == 0) return RD_OK;
     if (V == 0 || !unpacker || !packed_len || !packed_tokens || !logits || !q || !u_accept || !u_bonus ||
@@ -240,9 +245,10 @@ int rd_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *pack
         return RD_E_ARG;
     if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
     if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
+    if (ws_bytes < rd::stochastic_workspace_bytes(B, W, L) || !ws) return RD_E_WORKSPACE;
     return hip_status(rd::launch_stochastic_accept(dtype, unpacker, packed_len, packed_tokens, logits, q, u_accept,
                                                    u_bonus, B, W, L, V, best_beam, accept_len, accepted_tokens, path,
-                                                   as_stream(stream)));
+                                                   ws, as_stream(stream)));
 }
 
 int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,

@@ -73,10 +73,11 @@ hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best
                          hipStream_t stream, const PagedKV *paged = nullptr);
 
 // stochastic verification (multi-step speculative sampling over the tree)
+size_t stochastic_workspace_bytes(int B, int W, int L);
 hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *plen, const int32_t *ptok,
                                     const void *logits, const float *q, const float *u_accept, const float *u_bonus,
                                     int B, int W, int L, int V, int32_t *best_beam, int32_t *accept_len,
-                                    int32_t *accepted, int32_t *path, hipStream_t stream);
+                                    int32_t *accepted, int32_t *path, void *ws, hipStream_t stream);
 
 int device_cu_count();
 

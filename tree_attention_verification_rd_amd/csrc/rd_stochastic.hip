@@ -5,22 +5,38 @@
 // when all are rejected samples what remains of p, matching the target's
 // sampling distribution).
 //
-// One 1024-thread workgroup per request walks the tree from slot 0.  At
-// node u, p0 = softmax(logits[u]) is never stored: its max and sum are
-// reduced once and p0(x) recomputed where needed.  All children of u share
-// q = q[u], so the residual after i rejections has the closed form
+// p0 = softmax(logits[u]) is never stored: its max and sum are reduced and
+// p0(x) recomputed where needed.  All children of node u share q = q[u], so
+// the residual after i rejections has the closed form
 // p_i = max(p0 - c_i q, 0) / D_i, with c_0 = 0, D_0 = 1 and, after a
 // rejection, c <- c + D, D <- sum max(p0 - c q, 0) (kept when that sum is
 // 0): by induction max(p_i - q, 0) = max(p0 - (c_i + D_i) q, 0) / D_i, the
-// rows where p0 <= c_i q staying zero.  So a rejection costs one read-only
-// reduction and no rewrite of a vector.  Children of u (slots whose parent
-// is u, all above u) are found in slot order by a block-wide scan of a flag
-// per slot; each is tested with u_accept * q(x) < p_i(x).  With no child
-// accepted (or at a leaf) the bonus token is the first index whose running
-// sum of max(p0 - c q, 0) exceeds u_bonus times its total: each thread sums
-// a contiguous segment, one block scan orders the segments, and the thread
-// whose segment holds the crossing finds it.  All sums run in a fixed
-// order, so results are deterministic.
+// rows where p0 <= c_i q staying zero.  The sequence (c_i, D_i) of a node
+// depends on its p0 and q only, not on the uniforms, so it is computed for
+// every node at once:
+//   k_stoch_node  -- one workgroup per (request, slot): the max and sum of
+//                    the slot's logits, (c_i, D_i) for i up to its child
+//                    count nk, the pair (p_i(x), q(x)) that its i-th child
+//                    (token x) is tested with, stored with that child, and
+//                    the bonus token the slot yields if every child is
+//                    rejected: the first index whose running sum of
+//                    w = max(p0 - c_nk q, 0) exceeds u_bonus times its total.
+//                    Up to 32K entries the row stays in registers (thread t
+//                    holds x = t + 1024 j); the sums of the 32 "rows" j come
+//                    from a butterfly reduce-scatter per wave, a scan over
+//                    them picks the row holding the crossing, one block scan
+//                    finds it there.  Longer rows are streamed: each wave
+//                    takes a contiguous range with coalesced loads;
+//   k_stoch_walk  -- one workgroup per request: the pairs and the request's
+//                    uniforms are staged in LDS; from slot 0, children
+//                    (slots whose parent is the node, all above it) are
+//                    found in slot order by a block-wide scan of a flag per
+//                    slot and the i-th is accepted when u_accept * q(x) <
+//                    p_i(x); the node where every child is rejected (or a
+//                    leaf) gives its precomputed bonus.
+// Every block of the grid does the work of one row, so the chip's
+// bandwidth, not one CU's, bounds the pass over the logits.
+// All sums run in a fixed order, so results are deterministic.
 #include <math.h>
 
 #include "rd_common.h"
@@ -42,6 +58,8 @@ struct StochArgs {
     const float *u_bonus;
     int W, L, V, is_bf16;
     int32_t *best_beam, *accept_len, *accepted, *path;
+    float2 *test;    // [B,P]: (p_i(x), q(x)) of the slot's test at its parent (x its token, i its rank)
+    int32_t *bonus;  // [B,P]: the slot's bonus token when all its children are rejected
 };
 
 __device__ __forceinline__ float load_logit(const StochArgs &a, size_t i) {
@@ -76,6 +94,34 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 #pragma unroll
     for (int w = 0; w < kNW; ++w) t = fmaxf(t, red[w]);
     return t;
+}
+
+// (max, sum of exp(l - max)) of the block from each thread's pair (online
+// softmax: two pairs merge as M = max, s = s1 e^(m1-M) + s2 e^(m2-M)).
+// red is LDS scratch of 2 kNW floats.  Returns M; S in *S.
+__device__ __forceinline__ float merge_scale(float m, float M) { return m == -INFINITY ? 0.f : __expf(m - M); }
+__device__ __forceinline__ float block_softmax_stats(float m, float s, float *red, float *S) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float mo = shfl_xor(m, off), so = shfl_xor(s, off);
+        const float M = fmaxf(m, mo);
+        s = s * merge_scale(m, M) + so * merge_scale(mo, M);
+        m = M;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6] = m;
+        red[kNW + (threadIdx.x >> 6)] = s;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, red[w]);
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) t += red[kNW + w] * merge_scale(red[w], M);
+    *S = t;
+    return M;
 }
 
 // Inclusive block scan of one float per thread; returns the thread's
@@ -137,15 +183,347 @@ __device__ __forceinline__ void row_pass(const StochArgs &a, size_t lrow, const 
     }
 }
 
-__global__ __launch_bounds__(kT) void k_stochastic_accept(StochArgs a) {
+// This thread's elements x = tid + kT*j (j < RJ) of a row, by buffer loads:
+// one address register serves all of them (the step is a scalar offset) and
+// reads past the row's end give zero.
+template <int RJ>
+__device__ __forceinline__ void load_row_regs(const StochArgs &a, size_t lrow, float (&lv)[RJ], float (&qv)[RJ]) {
+    const uint32_t V = static_cast<uint32_t>(a.V), t = threadIdx.x;
+    const rsrc_t rq = make_rsrc(a.q + lrow, V * 4u);
+    if (a.is_bf16) {
+        const rsrc_t rl = make_rsrc(static_cast<const uint16_t *>(a.logits) + lrow, V * 2u);
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rl, t * 2u, kT * 2 * j, 0);
+            lv[j] = __uint_as_float(h << 16);
+        }
+    } else {
+        const rsrc_t rl = make_rsrc(static_cast<const float *>(a.logits) + lrow, V * 4u);
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, t * 4u, kT * 4 * j, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) qv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, t * 4u, kT * 4 * j, 0));
+}
+
+// parent slot of every slot of request b (-1 for roots), into LDS
+__device__ __forceinline__ void build_parents(const StochArgs &a, int b, int n, int *parent) {
+    const int P = a.W * a.L;
+    const int32_t *un = a.unpacker + static_cast<size_t>(b) * P;
+    for (int i = threadIdx.x; i < P; i += kT) parent[i] = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < P; i += kT) {
+        const int l = i % a.L;
+        const int c = un[i];
+        if (l > 0 && c >= 0 && c < n) parent[c] = un[i - 1];
+    }
+    __syncthreads();
+}
+
+// children of slot u in slot order into kids (at most kMaxBeams); returns their count
+__device__ __forceinline__ int children_of(int u, int n, const int *parent, int *kids, int *redi, int *cnt_sh) {
+    const int cs = threadIdx.x;
+    const int flag = (cs > u && cs < n && parent[cs] == u) ? 1 : 0;
+    int tot;
+    const int r = block_count_scan(flag, redi, tot);
+    if (flag && r < kMaxBeams) kids[r] = cs;
+    if (threadIdx.x == 0) *cnt_sh = min(tot, kMaxBeams);
+    __syncthreads();
+    return *cnt_sh;
+}
+
+// Bonus of a register-resident row: thread t holds p0 and q of
+// x = t + kT*j in pv[j], qv[j] (zeros past the row), so the weight of x is
+// max(pv[j] - c qv[j], 0).  Returns, in every thread, the first x whose
+// running sum in x order exceeds u_b times the total.  When rounding between
+// the two levels hides the crossing, or u_b * total rounds up to the total,
+// the last index of nonzero weight stands in (where the crossing lies in
+// exact arithmetic).
+template <int RJ>
+__device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&qv)[RJ], float c, float u_b,
+                                          float *red, int *redi, float (*rows)[RJ], float *sh_f, int *sh_i) {
+    static_assert(RJ == 32, "the reduce-scatter below halves 32 rows over lane bits 5..1");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    auto wt = [&](int j) { return fmaxf(pv[j] - c * qv[j], 0.f); };
+    // Row sums by reduce-scatter: the step on lane bit m keeps the half of
+    // the rows that bit selects, adding the partner's copy of them; lane l
+    // ends with row l >> 1 of the wave, and a last step adds lanes l, l^1.
+    float h[16];
+    {
+        const bool up = lane & 32;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float lo = wt(k), hi = wt(k + 16);
+            h[k] = (up ? hi : lo) + shfl_xor(up ? lo : hi, 32);
+        }
+    }
+#pragma unroll
+    for (int half = 8, m = 16; half >= 1; half >>= 1, m >>= 1) {
+        const bool up = lane & m;
+#pragma unroll
+        for (int k = 0; k < half; ++k) h[k] = (up ? h[k + half] : h[k]) + shfl_xor(up ? h[k] : h[k + half], m);
+    }
+    h[0] += shfl_xor(h[0], 1);
+    if (!(lane & 1)) rows[wave][lane >> 1] = h[0];
+    __syncthreads();
+    if (wave == 0) {
+        float R = 0.f;
+        if (lane < RJ)
+            for (int w2 = 0; w2 < kNW; ++w2) R += rows[w2][lane];
+        float I = R;  // inclusive scan of the row sums
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(I, off, 64);
+            if (lane >= off) I += o;
+        }
+        const float up1 = __shfl_up(I, 1, 64);
+        const float E = lane ? up1 : 0.f;
+        const float thr = u_b * __shfl(I, 63, 64);
+        const uint64_t hit = __ballot(lane < RJ && I > thr);
+        const uint64_t nz = __ballot(lane < RJ && R > 0.f);
+        const int js = hit ? __ffsll(static_cast<long long>(hit)) - 1
+                           : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
+        if (lane == js) {
+            sh_i[0] = js;
+            sh_i[1] = hit ? 1 : 0;
+            sh_f[0] = E;
+            sh_f[1] = thr;
+        }
+    }
+    __syncthreads();
+    const int js = sh_i[0];
+    const bool exact = sh_i[1] != 0;
+    const float E = sh_f[0], thr = sh_f[1];
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j)
+        if (j == js) v = wt(j);
+    float tot;
+    const float inc = block_scan(v, red, tot);
+    const uint64_t hit = __ballot(exact && E + inc > thr);
+    const uint64_t nz = __ballot(v > 0.f);
+    if (lane == 0) {
+        redi[wave] = hit ? wave * 64 + __ffsll(static_cast<long long>(hit)) - 1 : kT;
+        redi[kNW + wave] = nz ? wave * 64 + 63 - __clzll(static_cast<long long>(nz)) : -1;
+    }
+    __syncthreads();
+    int first = kT, last = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+        first = min(first, redi[w2]);
+        last = max(last, redi[kNW + w2]);
+    }
+    return (first < kT ? first : last) + kT * js;
+}
+
+// Bonus of a streamed row (p0 = exp(l - M) * invS, weight max(p0 - c q, 0)):
+// wave wv owns the contiguous range [wv*RW, (wv+1)*RW) and reads it 64
+// entries a step.  A range whose running sum already exceeds the threshold at
+// its start proposes its first index, so rounding between ranges cannot hide
+// the crossing; the lowest proposal wins, and with none the last index of
+// nonzero weight stands in.  Result valid in every thread.
+__device__ __forceinline__ int bonus_streamed(const StochArgs &a, size_t lrow, const float *qrow, float M, float invS,
+                                              float c, float u_b, float *red, int *redi) {
+    const int V = a.V;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int RW = (V + kNW - 1) / kNW;
+    const int r0 = min(wv * RW, V), r1 = min(r0 + RW, V);
+    const int nsteps = (r1 - r0 + 63) / 64;
+    constexpr int kSB = 16;  // steps loaded together
+    auto step_weights = [&](int s0, float (&w)[kSB]) {
+        float lv[kSB], qv[kSB];
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+            const int x = min(r0 + (s0 + j) * 64 + lane, max(r1 - 1, 0));
+            lv[j] = load_logit(a, lrow + x);
+            qv[j] = qrow[x];
+        }
+#pragma unroll
+        for (int j = 0; j < kSB; ++j)
+            w[j] = (r0 + (s0 + j) * 64 + lane < r1) ? fmaxf(__expf(lv[j] - M) * invS - c * qv[j], 0.f) : 0.f;
+    };
+    float lsum = 0.f;
+    int lastnz = -1;
+    for (int s0 = 0; s0 < nsteps; s0 += kSB) {
+        float w[kSB];
+        step_weights(s0, w);
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+            lsum += w[j];
+            if (w[j] > 0.f) lastnz = r0 + (s0 + j) * 64 + lane;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        lsum += shfl_xor(lsum, off);  // the wave's total, in every lane
+        lastnz = max(lastnz, shfl_xor(lastnz, off));
+    }
+    __syncthreads();
+    if (lane == 0) {
+        red[wv] = lsum;
+        redi[kNW + wv] = lastnz;
+    }
+    __syncthreads();
+    float exc = 0.f, total = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+        if (w2 < wv) exc += red[w2];
+        total += red[w2];
+    }
+    const float thr = u_b * total;
+    int cand = V;
+    if (r0 < r1) {
+        if (exc > thr) {
+            cand = r0;
+        } else {
+            float carry = exc;
+            for (int s0 = 0; s0 < nsteps && cand == V; s0 += kSB) {
+                float w[kSB];
+                step_weights(s0, w);
+#pragma unroll
+                for (int j = 0; j < kSB; ++j) {
+                    float inc = w[j];
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float o = __shfl_up(inc, off, 64);
+                        if (lane >= off) inc += o;
+                    }
+                    const float tot = __shfl(inc, 63, 64);
+                    const uint64_t hit = __ballot(carry + inc > thr && r0 + (s0 + j) * 64 + lane < r1);
+                    if (cand == V && hit) cand = r0 + (s0 + j) * 64 + __ffsll(static_cast<long long>(hit)) - 1;
+                    carry += tot;
+                }
+            }
+        }
+    }
+    if (lane == 0) redi[wv] = cand;
+    __syncthreads();
+    int first = V, last = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+        first = min(first, redi[w2]);
+        last = max(last, redi[kNW + w2]);
+    }
+    return first < V ? first : last;
+}
+
+// Every statistic of one slot: (max, 1/sum) of its logits, the residual
+// sequence (c_i, D_i) for i up to its child count, each child's test pair
+// and the slot's bonus.  With RJ > 0 (V <= kT * RJ) the slot's logits and q
+// are loaded once into registers (element x = tid + kT*j) and every pass runs
+// on them; with RJ == 0 each pass streams the row.
+template <int RJ>
+__global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     __shared__ int parent[kMaxSlots];
     __shared__ int kids[kMaxBeams];
-    __shared__ float red[kNW];
+    __shared__ float2 cd_sh[kMaxBeams];
+    __shared__ float red[2 * kNW];
+    __shared__ int redi[2 * kNW];
+    __shared__ int tok_sh[kMaxSlots];
+    __shared__ float rows[kNW][RJ > 0 ? RJ : 1];
+    __shared__ float sh_f[2];
+    __shared__ int sh_i[2];
+    __shared__ int nkids_sh;
+    const int W = a.W, L = a.L, V = a.V;
+    const int P = W * L;
+    const int b = blockIdx.x / P;
+    const int u = blockIdx.x % P;
+    const int n = min(max(a.plen[b], 0), P);
+    if (u >= n) return;
+    const size_t ubase = static_cast<size_t>(b) * P;
+    const size_t lrow = (ubase + u) * static_cast<size_t>(V);
+    const float *qrow = a.q + lrow;
+    float pv[RJ > 0 ? RJ : 1], qv[RJ > 0 ? RJ : 1];  // logits, then p0, and q of this thread's elements
+    if constexpr (RJ > 0) load_row_regs<RJ>(a, lrow, pv, qv);  // issued first: the loads overlap the tree build
+    if (static_cast<int>(threadIdx.x) < n) tok_sh[threadIdx.x] = a.ptok[ubase + threadIdx.x];
+    build_parents(a, b, n, parent);  // its barriers also publish tok_sh
+    const int nk = children_of(u, n, parent, kids, redi, &nkids_sh);
+    // thread i < nk: child i's token, its logit and q (their latency hides
+    // behind the softmax statistics)
+    int kid = -1;
+    float kl = 0.f, kq = 0.f;
+    if (static_cast<int>(threadIdx.x) < nk) {
+        kid = kids[threadIdx.x];
+        const int x = min(max(tok_sh[kid], 0), V - 1);
+        kl = load_logit(a, lrow + x);
+        kq = qrow[x];
+    }
+    // softmax statistics: from registers, the block max then the sum of
+    // exp(l - M) (one exponential per entry); streamed, one pass of per-thread
+    // (max, sum) pairs merged across the block
+    float M, invS;
+    if constexpr (RJ > 0) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < RJ; ++j)
+            if (static_cast<int>(threadIdx.x) + kT * j < V) m = fmaxf(m, pv[j]);
+        M = block_max(m, red);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const bool ok = static_cast<int>(threadIdx.x) + kT * j < V;
+            pv[j] = ok ? __expf(pv[j] - M) : 0.f;
+            qv[j] = ok ? qv[j] : 0.f;
+            s += pv[j];
+        }
+        invS = 1.f / block_sum(s, red);
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) pv[j] *= invS;
+    } else {
+        float m = -INFINITY, s = 0.f;
+        row_pass(a, lrow, nullptr, V, [&](int, float l, float) {
+            const float mn = fmaxf(m, l);
+            s = s * merge_scale(m, mn) + __expf(l - mn);
+            m = mn;
+        });
+        float S;
+        M = block_softmax_stats(m, s, red, &S);
+        invS = 1.f / S;
+    }
+    if (threadIdx.x == 0) cd_sh[0] = make_float2(0.f, 1.f);
+    float c = 0.f, D = 1.f;
+    for (int i = 0; i < nk; ++i) {
+        const float cn = c + D;
+        float t = 0.f;
+        if constexpr (RJ > 0) {
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) t += fmaxf(pv[j] - cn * qv[j], 0.f);
+        } else {
+            row_pass(a, lrow, qrow, V,
+                     [&](int, float l, float q1) { t += fmaxf(__expf(l - M) * invS - cn * q1, 0.f); });
+        }
+        const float T = block_sum(t, red);
+        if (T > 0.f) {
+            c = cn;
+            D = T;
+        }
+        if (threadIdx.x == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
+    }
+    __syncthreads();
+    if (kid >= 0) {
+        const float2 cd = cd_sh[threadIdx.x];
+        const float px = fmaxf(__expf(kl - M) * invS - cd.x * kq, 0.f) / cd.y;
+        a.test[ubase + kid] = make_float2(px, kq);
+    }
+    const float ub = a.u_bonus[b];
+    int bonus;
+    if constexpr (RJ > 0)
+        bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, rows, sh_f, sh_i);
+    else
+        bonus = bonus_streamed(a, lrow, qrow, M, invS, c, ub, red, redi);
+    if (threadIdx.x == 0) a.bonus[ubase + u] = min(bonus, V - 1);
+}
+
+__global__ __launch_bounds__(kT) void k_stoch_walk(StochArgs a) {
+    __shared__ int parent[kMaxSlots];
+    __shared__ float2 test_sh[kMaxSlots];  // (p_i(x), q(x)) of each slot's test at its parent
+    __shared__ float ua_sh[kMaxBeamLen * kMaxBeams];
+    __shared__ int kids[kMaxBeams];
     __shared__ int redi[kNW];
     __shared__ int nkids_sh;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int W = a.W, L = a.L, V = a.V;
+    const int W = a.W, L = a.L;
     const int P = W * L;
     const int n = min(max(a.plen[b], 0), P);
     int32_t *acc_row = a.accepted + static_cast<size_t>(b) * L;
@@ -161,149 +539,66 @@ __global__ __launch_bounds__(kT) void k_stochastic_accept(StochArgs a) {
         }
         return;
     }
-    // parent of every slot (the same for every candidate that maps to it)
     const int32_t *un = a.unpacker + static_cast<size_t>(b) * P;
-    for (int i = tid; i < P; i += kT) parent[i] = -1;
-    __syncthreads();
-    for (int i = tid; i < P; i += kT) {
-        const int l = i % L;
-        const int c = un[i];
-        if (l > 0 && c >= 0 && c < n) parent[c] = un[i - 1];
-    }
-    __syncthreads();
-
     const size_t ubase = static_cast<size_t>(b) * P;
-    int u = 0, d = 0, nacc = 0;
-    float M = 0.f, invS = 1.f, c = 0.f;  // p0 = exp(l - M) * invS at node u; residual offset c
-    size_t lrow = 0;
-    const float *qrow = nullptr;
-    auto p0v = [&](float l) { return __expf(l - M) * invS; };
-    if (tid == 0 && path_row) path_row[0] = 0;
+    for (int i = tid; i < n; i += kT) test_sh[i] = a.test[ubase + i];
+    for (int i = tid; i < L * W; i += kT) ua_sh[i] = a.u_acc[static_cast<size_t>(b) * L * W + i];
+    build_parents(a, b, n, parent);  // its barriers also publish the staging above
+    int u = 0, d = 0;
     while (true) {
-        lrow = (ubase + u) * static_cast<size_t>(V);
-        qrow = a.q + (ubase + u) * static_cast<size_t>(V);
-        float m = -INFINITY;
-        row_pass(a, lrow, nullptr, V, [&](int, float l, float) { m = fmaxf(m, l); });
-        M = block_max(m, red);
-        float s = 0.f;
-        row_pass(a, lrow, nullptr, V, [&](int, float l, float) { s += __expf(l - M); });
-        invS = 1.f / block_sum(s, red);
-        c = 0.f;
-        float D = 1.f;
-        // children of u in slot order
-        int nk;
-        {
-            const int cs = tid;
-            const int flag = (cs > u && cs < n && parent[cs] == u) ? 1 : 0;
-            int tot;
-            const int r = block_count_scan(flag, redi, tot);
-            if (flag && r < kMaxBeams) kids[r] = cs;
-            if (tid == 0) nkids_sh = min(tot, kMaxBeams);
-            __syncthreads();
-            nk = nkids_sh;
-        }
+        // a node at depth L-1 is a leaf (bounds the walk on any unpacker)
+        const int nk = d + 1 < L ? children_of(u, n, parent, kids, redi, &nkids_sh) : 0;
         int next = -1;
         for (int i = 0; i < nk; ++i) {
             const int ch = kids[i];
-            const int x = min(max(a.ptok[ubase + ch], 0), V - 1);
-            const float r = a.u_acc[(static_cast<size_t>(b) * L + d) * W + min(i, W - 1)];
-            const float px = fmaxf(p0v(load_logit(a, lrow + x)) - c * qrow[x], 0.f) / D;
-            if (r * qrow[x] < px) {  // the same values in every thread: a uniform branch
+            const float r = ua_sh[d * W + min(i, W - 1)];
+            const float2 t = test_sh[ch];
+            if (r * t.y < t.x) {  // the same values in every thread: a uniform branch
                 next = ch;
                 break;
-            }
-            const float cn = c + D;
-            float t = 0.f;
-            row_pass(a, lrow, qrow, V, [&](int, float l, float qv) { t += fmaxf(p0v(l) - cn * qv, 0.f); });
-            const float T = block_sum(t, red);
-            if (T > 0.f) {
-                c = cn;
-                D = T;
             }
         }
         if (next < 0) break;
         if (tid == 0) {
-            acc_row[nacc] = a.ptok[ubase + next];
+            acc_row[d] = a.ptok[ubase + next];
             if (path_row) path_row[d + 1] = next;
         }
         u = next;
         ++d;
-        ++nacc;
     }
-    // bonus: first index whose running sum of max(p0 - c q, 0) exceeds
-    // u_bonus times the total; thread t owns the contiguous segment
-    // [t*seg, (t+1)*seg)
-    const int seg = (V + kT - 1) / kT;
-    const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
-    // weights of a batch of the thread's segment (loads issued together)
-    auto seg_batch = [&](int xb, float (&wv)[kUB]) {
-        float lv[kUB], qv[kUB];
-#pragma unroll
-        for (int j = 0; j < kUB; ++j) {
-            const int x = min(xb + j, x1 - 1);
-            lv[j] = load_logit(a, lrow + x);
-            qv[j] = qrow[x];
-        }
-#pragma unroll
-        for (int j = 0; j < kUB; ++j) wv[j] = (xb + j < x1) ? fmaxf(p0v(lv[j]) - c * qv[j], 0.f) : 0.f;
-    };
-    float part = 0.f;
-    for (int xb = x0; xb < x1; xb += kUB) {
-        float wv[kUB];
-        seg_batch(xb, wv);
-#pragma unroll
-        for (int j = 0; j < kUB; ++j) part += wv[j];
-    }
-    float total;
-    const float exc = block_scan(part, red, total) - part;
-    const float thr = a.u_bonus[b] * total;
-    // a segment whose running sum already exceeds the threshold at its start
-    // proposes its first index, so rounding between segments cannot hide the
-    // crossing; the lowest proposal wins
-    int cand = V;
-    if (x0 < x1) {
-        if (exc > thr) {
-            cand = x0;
-        } else {
-            float acc = exc;
-            for (int xb = x0; xb < x1 && cand == V; xb += kUB) {
-                float wv[kUB];
-                seg_batch(xb, wv);
-#pragma unroll
-                for (int j = 0; j < kUB; ++j) {
-                    acc += wv[j];
-                    if (cand == V && xb + j < x1 && acc > thr) cand = xb + j;
-                }
-            }
-        }
-    }
-    // lowest candidate over the workgroup
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off, 64));
-    __syncthreads();
-    if ((tid & 63) == 0) redi[tid >> 6] = cand;
-    __syncthreads();
     if (tid == 0) {
-        int bonus = V;
-        for (int w = 0; w < kNW; ++w) bonus = min(bonus, redi[w]);
-        acc_row[nacc] = min(bonus, V - 1);
-        a.accept_len[b] = nacc;
+        if (path_row) path_row[0] = 0;
+        acc_row[d] = a.bonus[ubase + u];
+        a.accept_len[b] = d;
         int best = -1;
         for (int w = 0; w < W && best < 0; ++w)
-            if (un[w * L + nacc] == u) best = w;
+            if (un[w * L + d] == u) best = w;
         a.best_beam[b] = best;
     }
 }
 
 }  // namespace
 
+size_t stochastic_workspace_bytes(int B, int W, int L) {
+    const size_t slots = static_cast<size_t>(B) * W * L;
+    return slots * (sizeof(float2) + sizeof(int32_t));
+}
+
 hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *plen, const int32_t *ptok,
                                     const void *logits, const float *q, const float *u_accept, const float *u_bonus,
                                     int B, int W, int L, int V, int32_t *best_beam, int32_t *accept_len,
-                                    int32_t *accepted, int32_t *path, hipStream_t stream) {
+                                    int32_t *accepted, int32_t *path, void *ws, hipStream_t stream) {
     StochArgs a{unpacker, plen, ptok, logits, q, u_accept, u_bonus, W, L, V, dtype == 1 ? 1 : 0,
-                best_beam, accept_len, accepted, path};
-    hipLaunchKernelGGL(k_stochastic_accept, dim3(B), dim3(kT), 0, stream, a);
+                best_beam, accept_len, accepted, path, static_cast<float2 *>(ws),
+                reinterpret_cast<int32_t *>(static_cast<float2 *>(ws) + static_cast<size_t>(B) * W * L)};
+    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * W * L));
+    if (V <= kT * 32)
+        hipLaunchKernelGGL(k_stoch_node<32>, grid, dim3(kT), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_stoch_node<0>, grid, dim3(kT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_stoch_walk, dim3(B), dim3(kT), 0, stream, a);
     return hipGetLastError();
 }
 
