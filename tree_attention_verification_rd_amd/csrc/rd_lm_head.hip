@@ -101,7 +101,7 @@ __device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32
     }
 }
 
-template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK>
+template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK, bool KROT>
 __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     static_assert(GV * GR == 4, "four wavefronts per workgroup");
     static_assert(NSX >= 2 && NSW >= NSX, "each ring needs a stage in flight while another is consumed");
@@ -163,10 +163,11 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     const uint32_t boff = static_cast<uint32_t>(gr * WR + lq) * kRowB + sw;
     // All workgroups on one XCD (block i runs on XCD i % 8) walk K in the
     // same order and mostly run side by side, so the rows they share are
-    // fetched into that XCD's L2 once; the XCDs start at different k-steps
-    // so that they do not all address the same offset of the power-of-two-
-    // strided rows at once (which would crowd a few HBM channels).
-    const int krot = ((blockIdx.x & 7) * nk / 8) % nk;
+    // fetched into that XCD's L2 once.  With KROT the XCDs start at
+    // different k-steps, so that they do not all address the same offset of
+    // the power-of-two-strided rows at once; the few-row shape (one tile per
+    // CU, every CU streaming its own weight rows) measured faster without.
+    const int krot = KROT ? ((blockIdx.x & 7) * nk / 8) % nk : 0;
 
     // The grid is sized on the host for the largest possible row count, but
     // only tiles with valid rows do work.  The first ntiles workgroups take
@@ -246,20 +247,17 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         //
         // Fragments are software-pipelined across the barrier: the last
         // 32-wide MFMA step of k-step kt is read into registers before the
-        // barrier of k-step kt+1 and multiplied after it, while the first
-        // reads of k-step kt+1 are in flight, so LDS latency does not stall
-        // the MFMAs.  (The first k-step multiplies zero fragments in that
-        // slot.)  With one MFMA step per k-step the two fragment buffers
+        // barrier of k-step kt+1 and multiplied after it, so LDS latency does
+        // not stall the MFMAs.  (The first k-step multiplies zero fragments in
+        // that slot.)  With one MFMA step per k-step the two fragment buffers
         // alternate between k-steps.
-        auto read_frags = [&](const uint8_t *wst, const uint8_t *xst, uint32_t x, bf16x8 (&fa)[NVB],
-                              bf16x8 (&fb)[NRB]) {
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb)
-                fa[vb] = *reinterpret_cast<const bf16x8 *>(wst + ((aoff ^ x) + vb * 16 * kRowB));
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                fb[rb] = *reinterpret_cast<const bf16x8 *>(xst + ((boff ^ x) + rb * 16 * kRowB));
-        };
+        //
+        // Within a k-step the multiplies run in chunks, and the ring loads and
+        // fragment reads are spread between the chunks.  Issued as one burst
+        // after the barrier, they kept the single wavefront of each SIMD from
+        // issuing MFMAs until the burst had been accepted: per-k-step stamps
+        // showed the loads costing 400-500 cycles on top of ~1200 cycles of
+        // multiplies.
         auto mma = [&](const bf16x8 (&fa)[NVB], const bf16x8 (&fb)[NRB]) {
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb)
@@ -287,27 +285,50 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             constexpr int cur = decltype(cur_c)::value;  // fragment buffer of this k-step
             vm_wait<(NSX - 2) * NL>();
             __syncthreads();
-            issue_w(kt + NSW - 1, (wslot == 0) ? NSW - 1 : wslot - 1);  // slot (kt + NSW - 1) % NSW
-            issue_x(kt + NSX - 1, (xslot == 0) ? NSX - 1 : xslot - 1);
+            // this k-step's loads: weight stage kt+NSW-1, hidden stage kt+NSX-1
+            const int krw = kstep_of(kt + NSW - 1), krx = kstep_of(kt + NSX - 1);
+            const bool kinw = krw >= 0 && krw * BK + 8 * lchunk < K;
+            const bool kinx = krx >= 0 && krx * BK + 8 * lchunk < K;
+            const uint32_t kaddw = static_cast<uint32_t>(krw) * kRowB, kaddx = static_cast<uint32_t>(krx) * kRowB;
+            const int wsl = (wslot == 0) ? NSW - 1 : wslot - 1, xsl = (xslot == 0) ? NSX - 1 : xslot - 1;
+            const uint32_t sbw = lds0 + wsl * kWStage + wave * 1024;
+            const uint32_t sbx = lds0 + kXBase + xsl * kXStage + wave * 1024;
+            auto issue_one = [&](int j) {
+                if (j < NLW)
+                    lds_dma16(sbw + j * 4096, wres, kinw ? wbase + j * 4 * RPL * rowb + kaddw : kOOB);
+                else
+                    lds_dma16(sbx + (j - NLW) * 4096, xres, kinx ? xbase[j - NLW] + kaddx : kOOB);
+            };
             if (active) {
                 const uint8_t *wst = lds + wslot * kWStage;
                 const uint8_t *xst = lds + kXBase + xslot * kXStage;
-                if constexpr (NSUB == 2) {
-                    read_frags(wst, xst, 0u, fa2[0], fb2[0]);
-                    mma(fa2[1], fb2[1]);
-                    read_frags(wst, xst, 64u, fa2[1], fb2[1]);
-                    mma(fa2[0], fb2[0]);
-                    // keep that order: reads, multiplies, reads, multiplies
-                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
-                } else {
-                    read_frags(wst, xst, 0u, fa2[cur], fb2[cur]);
-                    mma(fa2[cur ^ 1], fb2[cur ^ 1]);
-                    __builtin_amdgcn_sched_group_barrier(0x100, NVB + NRB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, NVB * NRB, 0);
+                // The multiplies run in NSUB*NVB chunks of NRB; the loads and
+                // this k-step's fragment reads are spread between the chunks
+                // so that the MFMA pipe always has work queued.
+                constexpr int NCH = NSUB * NVB;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int h = c / NVB, vb = c % NVB;
+#pragma unroll
+                    for (int j = c * NL / NCH; j < (c + 1) * NL / NCH; ++j) issue_one(j);
+                    // the fragments this chunk multiplies: NSUB == 1, the held
+                    // buffer; NSUB == 2, half 0 the held second half of the
+                    // previous k-step, half 1 this k-step's first half
+                    const int src = (NSUB == 2) ? (h == 0 ? 1 : 0) : (cur ^ 1);
+                    const int dst = (NSUB == 2) ? (h == 0 ? 0 : 1) : cur;
+                    const uint32_t x = (NSUB == 2 && h == 1) ? 64u : 0u;
+                    fa2[dst][vb] = *reinterpret_cast<const bf16x8 *>(wst + ((aoff ^ x) + vb * 16 * kRowB));
+#pragma unroll
+                    for (int rb = vb * NRB / NVB; rb < (vb + 1) * NRB / NVB; ++rb)
+                        fb2[dst][rb] = *reinterpret_cast<const bf16x8 *>(xst + ((boff ^ x) + rb * 16 * kRowB));
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) acc[vb][rb] = mfma16x16x32(fa2[src][vb], fb2[src][rb], acc[vb][rb]);
+                    // keep the chunks in this order: nothing moves across
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NL; ++j) issue_one(j);
             }
             wslot = (wslot + 1 == NSW) ? 0 : wslot + 1;
             xslot = (xslot + 1 == NSX) ? 0 : xslot + 1;
@@ -553,9 +574,9 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.nrt = static_cast<int>((rows + plan.rtile - 1) / plan.rtile);
         const dim3 grid(static_cast<unsigned>(a.nrt * a.nvt));
         if (plan.variant == 0)
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64, false>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32, true>), grid, dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
