@@ -13,8 +13,9 @@
 // vocabulary entries of one row -- what the argmax epilogue and the logits
 // store want.  Both operands are staged through LDS by direct global->LDS
 // loads (no registers, whole cache lines per instruction) into a ring of
-// k-steps of 64, and each of the four wavefronts multiplies a 128 x WR
-// block out of LDS with v_mfma_f32_16x16x32_bf16.  The epilogue reduces
+// k-steps, and each of the four multiplying wavefronts computes a 128 x WR
+// block out of LDS with v_mfma_f32_16x16x32_bf16 (in the few-row shape four
+// further wavefronts issue the loads).  The epilogue reduces
 // (max, first index) over the tile's vocabulary range and writes one
 // partial per (row, vocabulary tile); a second kernel reduces the partials
 // in a fixed order.
@@ -51,9 +52,10 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// Block-wide inclusive prefix sum of one value per thread (256 threads);
-// `tot` receives the sum.  `scratch` holds 4 ints.
-__device__ __forceinline__ int block_scan256(int v, int *scratch, int &tot) {
+// Block-wide inclusive prefix sum of one value per thread (NT threads);
+// `tot` receives the sum.  `scratch` holds NT/64 ints.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int *scratch, int &tot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -65,7 +67,7 @@ __device__ __forceinline__ int block_scan256(int v, int *scratch, int &tot) {
     int before = 0;
     tot = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const int sw = scratch[w];
         before += (w < wave) ? sw : 0;
         tot += sw;
@@ -77,32 +79,40 @@ __device__ __forceinline__ int block_scan256(int v, int *scratch, int &tot) {
 // Valid rows (p < packed_len[b]) are numbered in (b, p) order -- the compact
 // rows.  Pass 1 counts them; pass 2 records, for compact rows r0 .. r0+n-1,
 // the packed row b*P + p each one stands for.
+template <int NT>
 __device__ int count_rows(const int32_t *plen, int B, int P, int *scratch) {
     int carry = 0;
-    for (int b0 = 0; b0 < B; b0 += 256) {
+    for (int b0 = 0; b0 < B; b0 += NT) {
         const int b = b0 + static_cast<int>(threadIdx.x);
         const int n = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
         int tot;
-        block_scan256(n, scratch, tot);
+        block_scan<NT>(n, scratch, tot);
         carry += tot;
     }
     return carry;
 }
+template <int NT>
 __device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32_t *rmap, int *scratch) {
     int carry = 0;
-    for (int b0 = 0; b0 < B; b0 += 256) {
+    for (int b0 = 0; b0 < B; b0 += NT) {
         const int b = b0 + static_cast<int>(threadIdx.x);
         const int cnt = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
         int tot;
-        const int start = carry + block_scan256(cnt, scratch, tot) - cnt;
+        const int start = carry + block_scan<NT>(cnt, scratch, tot) - cnt;
         const int lo = max(start, r0), hi = min(start + cnt, r0 + n);
         for (int m = lo; m < hi; ++m) rmap[m - r0] = b * P + (m - start);
         carry += tot;
     }
 }
 
-template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK, bool KROT>
-__global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
+// SPEC: eight wavefronts, two per SIMD -- wavefronts 0-3 only multiply,
+// wavefronts 4-7 only issue the ring loads.  A load stalled at issue (the
+// memory pipeline full) then holds up only its own wavefront, while the
+// SIMD's multiplying wavefront keeps the MFMA pipe fed.  Needs a wave tile
+// that fits 256 registers.
+template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK, bool KROT, bool SPEC>
+__global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) {
+    constexpr int NT = SPEC ? 512 : 256;
     static_assert(GV * GR == 4, "four wavefronts per workgroup");
     static_assert(NSX >= 2 && NSW >= NSX, "each ring needs a stage in flight while another is consumed");
     static_assert(BK == 32 || BK == 64, "one or two 32-wide MFMA steps per k-step");
@@ -123,11 +133,11 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     static_assert(BV % (4 * RPL) == 0 && BR % (4 * RPL) == 0, "each wavefront loads whole groups of both operands");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NSW * kWStage + NSX * kXStage];
     __shared__ int32_t rmap[BR];  // packed row (b*P + p) of each compact row of the tile
-    __shared__ int scan_tmp[4];
+    __shared__ int scan_tmp[NT / 64];
 
     // wave-uniform values are read into scalar registers explicitly so the
     // buffer resources built from them stay scalar (no per-lane loops)
-    const int R = __builtin_amdgcn_readfirstlane(count_rows(a.plen, a.B, a.P, scan_tmp));
+    const int R = __builtin_amdgcn_readfirstlane(count_rows<NT>(a.plen, a.B, a.P, scan_tmp));
     const int nrt = (R + BR - 1) / BR;       // row tiles that hold valid rows
     const int ntiles = nrt * a.nvt;
     const int tid = threadIdx.x;
@@ -135,8 +145,12 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     const int lane = tid & 63;
     const int lq = lane & 15;
     const int kg = lane >> 4;
-    const int gv = wave % GV;
-    const int gr = wave / GV;
+    const bool loader = SPEC && wave >= 4;   // issues loads only
+    const bool issues = !SPEC || loader;     // issues ring loads
+    const int cw = wave & 3;                 // index among the multiplying wavefronts
+    const int lw = wave & 3;                 // index among the loading wavefronts
+    const int gv = cw % GV;
+    const int gr = cw / GV;
     const int K = a.K;
     const int nk = (K + BK - 1) / BK;
     const uint32_t rowb = static_cast<uint32_t>(K) * 2;
@@ -165,8 +179,9 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
     // same order and mostly run side by side, so the rows they share are
     // fetched into that XCD's L2 once.  With KROT the XCDs start at
     // different k-steps, so that they do not all address the same offset of
-    // the power-of-two-strided rows at once; the few-row shape (one tile per
-    // CU, every CU streaming its own weight rows) measured faster without.
+    // the power-of-two-strided rows at once (which would crowd a few HBM
+    // channels).  Both launched shapes use it; a shape without it stays
+    // available for measurement.
     const int krot = KROT ? ((blockIdx.x & 7) * nk / 8) % nk : 0;
 
     // The grid is sized on the host for the largest possible row count, but
@@ -187,18 +202,18 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         const int vt = within / gsz;
         const int r0 = rt * BR;
         const int v0 = vt * BV;
-        map_rows(a.plen, a.B, a.P, r0, min(BR, R - r0), rmap, scan_tmp);
+        map_rows<NT>(a.plen, a.B, a.P, r0, min(BR, R - r0), rmap, scan_tmp);
         __syncthreads();
 
         const int wrows = max(0, min(a.V - v0, BV));
         const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(v0, a.V)) * K,
                                         static_cast<uint32_t>(wrows) * rowb);
         // weight rows past V fall outside wres; hidden rows past R get kOOB
-        const uint32_t wbase = static_cast<uint32_t>(RPL * wave + lrow) * rowb + 16 * lchunk;
+        const uint32_t wbase = static_cast<uint32_t>(RPL * lw + lrow) * rowb + 16 * lchunk;
         uint32_t xbase[NLX];
 #pragma unroll
         for (int i = 0; i < NLX; ++i) {
-            const int m = r0 + RPL * (4 * i + wave) + lrow;
+            const int m = r0 + RPL * (4 * i + lw) + lrow;
             xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
         }
         // The weight rows of k-step kt (k-step (kt + krot) mod nk) go to
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             const int kr = kstep_of(kt);
             const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
             const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
-            const uint32_t sbase = lds0 + slot * kWStage + wave * 1024;
+            const uint32_t sbase = lds0 + slot * kWStage + lw * 1024;
 #pragma unroll
             for (int i = 0; i < NLW; ++i)
                 lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 4 * RPL * rowb + kadd : kOOB);
@@ -221,13 +236,13 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             const int kr = kstep_of(kt);
             const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
             const uint32_t kadd = static_cast<uint32_t>(kr) * kRowB;
-            const uint32_t sbase = lds0 + kXBase + slot * kXStage + wave * 1024;
+            const uint32_t sbase = lds0 + kXBase + slot * kXStage + lw * 1024;
 #pragma unroll
             for (int i = 0; i < NLX; ++i)
                 lds_dma16(sbase + i * 4096, xres, kin ? xbase[i] + kadd : kOOB);
         };
         // a wavefront whose rows are all padding only helps with the loads
-        const bool active = r0 + gr * WR < R;
+        const bool active = !loader && r0 + gr * WR < R;
 
         f32x4 acc[NVB][NRB];
 #pragma unroll
@@ -270,12 +285,14 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) fb2[1][rb] = bf16x8{};
 
+        if (issues) {
 #pragma unroll
-        for (int s = 0; s < NSW - NSX; ++s) issue_w(s, s);
+            for (int s = 0; s < NSW - NSX; ++s) issue_w(s, s);
 #pragma unroll
-        for (int j = 0; j < NSX - 1; ++j) {
-            issue_w(j + NSW - NSX, j + NSW - NSX);
-            issue_x(j, j);
+            for (int j = 0; j < NSX - 1; ++j) {
+                issue_w(j + NSW - NSX, j + NSW - NSX);
+                issue_x(j, j);
+            }
         }
 
         // The k loop is unrolled by two (the fragment buffers alternate);
@@ -291,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
             const bool kinx = krx >= 0 && krx * BK + 8 * lchunk < K;
             const uint32_t kaddw = static_cast<uint32_t>(krw) * kRowB, kaddx = static_cast<uint32_t>(krx) * kRowB;
             const int wsl = (wslot == 0) ? NSW - 1 : wslot - 1, xsl = (xslot == 0) ? NSX - 1 : xslot - 1;
-            const uint32_t sbw = lds0 + wsl * kWStage + wave * 1024;
-            const uint32_t sbx = lds0 + kXBase + xsl * kXStage + wave * 1024;
+            const uint32_t sbw = lds0 + wsl * kWStage + lw * 1024;
+            const uint32_t sbx = lds0 + kXBase + xsl * kXStage + lw * 1024;
             auto issue_one = [&](int j) {
                 if (j < NLW)
                     lds_dma16(sbw + j * 4096, wres, kinw ? wbase + j * 4 * RPL * rowb + kaddw : kOOB);
@@ -309,8 +326,10 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     const int h = c / NVB, vb = c % NVB;
+                    if (!SPEC) {
 #pragma unroll
-                    for (int j = c * NL / NCH; j < (c + 1) * NL / NCH; ++j) issue_one(j);
+                        for (int j = c * NL / NCH; j < (c + 1) * NL / NCH; ++j) issue_one(j);
+                    }
                     // the fragments this chunk multiplies: NSUB == 1, the held
                     // buffer; NSUB == 2, half 0 the held second half of the
                     // previous k-step, half 1 this k-step's first half
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
                     // keep the chunks in this order: nothing moves across
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            } else {
+            } else if (issues) {
 #pragma unroll
                 for (int j = 0; j < NL; ++j) issue_one(j);
             }
@@ -347,66 +366,69 @@ __global__ __launch_bounds__(256, 1) void k_lm_head_bf16(LmArgs a) {
         //                                   vocab v0 + gv*WV + vb*16 + 4*kg + e)
         float *redv = reinterpret_cast<float *>(lds);
         int32_t *redi = reinterpret_cast<int32_t *>(lds + GV * BR * 4);
+        // the loading wavefronts hold no results
+        if (!loader) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const int row = gr * WR + rb * 16 + lq;
-            const int m = r0 + row;
-            const bool mvalid = m < R;
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            if (active) {
-                const int pr = mvalid ? rmap[m - r0] : 0;
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int row = gr * WR + rb * 16 + lq;
+                const int m = r0 + row;
+                const bool mvalid = m < R;
+                float bv = -INFINITY;
+                int bi = 0x7fffffff;
+                if (active) {
+                    const int pr = mvalid ? rmap[m - r0] : 0;
 #pragma unroll
-                for (int vb = 0; vb < NVB; ++vb) {
-                    const int v = v0 + gv * WV + vb * 16 + 4 * kg;
-                    // candidates come in increasing vocabulary order, so a
-                    // strict compare keeps the first of equal values
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const int v = v0 + gv * WV + vb * 16 + 4 * kg;
+                        // candidates come in increasing vocabulary order, so a
+                        // strict compare keeps the first of equal values
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool take = (v + e < a.V) & (acc[vb][rb][e] > bv);
-                        bv = take ? acc[vb][rb][e] : bv;
-                        bi = take ? v + e : bi;
-                    }
-                    if (a.logits && mvalid) {
-                        uint16_t *dst = a.logits + static_cast<size_t>(pr) * a.V + v;
-                        if (v + 3 < a.V && (a.V % 4 == 0)) {
-                            u16x4 w = {f32_to_bf16_bits(acc[vb][rb][0]), f32_to_bf16_bits(acc[vb][rb][1]),
-                                       f32_to_bf16_bits(acc[vb][rb][2]), f32_to_bf16_bits(acc[vb][rb][3])};
-                            *reinterpret_cast<u16x4 *>(dst) = w;
-                        } else {
+                        for (int e = 0; e < 4; ++e) {
+                            const bool take = (v + e < a.V) & (acc[vb][rb][e] > bv);
+                            bv = take ? acc[vb][rb][e] : bv;
+                            bi = take ? v + e : bi;
+                        }
+                        if (a.logits && mvalid) {
+                            uint16_t *dst = a.logits + static_cast<size_t>(pr) * a.V + v;
+                            if (v + 3 < a.V && (a.V % 4 == 0)) {
+                                u16x4 w = {f32_to_bf16_bits(acc[vb][rb][0]), f32_to_bf16_bits(acc[vb][rb][1]),
+                                           f32_to_bf16_bits(acc[vb][rb][2]), f32_to_bf16_bits(acc[vb][rb][3])};
+                                *reinterpret_cast<u16x4 *>(dst) = w;
+                            } else {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (v + e < a.V) dst[e] = f32_to_bf16_bits(acc[vb][rb][e]);
+                                for (int e = 0; e < 4; ++e)
+                                    if (v + e < a.V) dst[e] = f32_to_bf16_bits(acc[vb][rb][e]);
+                            }
                         }
                     }
                 }
-            }
 #pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                const float ov = shfl_xor(bv, off);
-                const int oi = shfl_xor(bi, off);
-                if (better(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (kg == 0) {
-                if (GV == 1) {
-                    if (mvalid) {
-                        const size_t pr = static_cast<size_t>(rmap[m - r0]);
-                        a.pval[pr * a.nvt + vt] = bv;
-                        a.pidx[pr * a.nvt + vt] = bi;
+                for (int off = 16; off <= 32; off <<= 1) {
+                    const float ov = shfl_xor(bv, off);
+                    const int oi = shfl_xor(bi, off);
+                    if (better(ov, oi, bv, bi)) {
+                        bv = ov;
+                        bi = oi;
                     }
-                } else {
-                    redv[gv * BR + row] = bv;
-                    redi[gv * BR + row] = bi;
+                }
+                if (kg == 0) {
+                    if (GV == 1) {
+                        if (mvalid) {
+                            const size_t pr = static_cast<size_t>(rmap[m - r0]);
+                            a.pval[pr * a.nvt + vt] = bv;
+                            a.pidx[pr * a.nvt + vt] = bi;
+                        }
+                    } else {
+                        redv[gv * BR + row] = bv;
+                        redi[gv * BR + row] = bi;
+                    }
                 }
             }
         }
         if (GV > 1) {
             __syncthreads();
             const int rvalid = min(BR, R - r0);
-            for (int i = tid; i < rvalid; i += 256) {
+            for (int i = tid; i < rvalid; i += NT) {
                 float bv = redv[i];
                 int bi = redi[i];
 #pragma unroll
@@ -528,12 +550,16 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
         plan.variant = 0;
     } else {
         // Two tile shapes.  Few rows (the weight stream dominates): 128
-        // vocabulary x 256 rows per tile, 128x64 per wavefront, k-steps of
-        // 64, three weight and three hidden stages -- twice as many tiles to
-        // spread over the CUs.  Many rows (the MFMAs dominate): 256 x 256 per
-        // tile, 128x128 per wavefront, k-steps of 32, five weight and four
-        // hidden stages -- a third less L2 traffic per flop.  (Ring depths
-        // measured on MI355X: deeper weight rings slow the few-row shape.)
+        // vocabulary x 256 rows per tile, 128x64 per multiplying wavefront,
+        // k-steps of 64, three weight and three hidden stages -- twice as many
+        // tiles to spread over the CUs -- with four more wavefronts that only
+        // issue the loads (measured at llama_mha size: 77-80 us against 89-94
+        // us with one wavefront per SIMD doing both).  Many rows (the MFMAs
+        // dominate): 256 x 256 per tile, 128x128 per wavefront (too many
+        // registers for a second wavefront per SIMD), k-steps of 32, five
+        // weight and four hidden stages -- a third less L2 traffic per flop.
+        // (Ring depths measured on MI355X: deeper weight rings slow the
+        // few-row shape.)
         // RD_LM_VARIANT forces one.
         const char *env = getenv("RD_LM_VARIANT");
         plan.variant = (env && *env) ? (atoi(env) != 0) : (plan.rows_pad > 512 ? 1 : 0);
@@ -574,9 +600,9 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.nrt = static_cast<int>((rows + plan.rtile - 1) / plan.rtile);
         const dim3 grid(static_cast<unsigned>(a.nrt * a.nvt));
         if (plan.variant == 0)
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64, true, true>), grid, dim3(512), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32, true, false>), grid, dim3(256), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
