@@ -66,6 +66,9 @@ CASES = {
     "llama_vocab": (8, 8, 5, 32000, "bf16", 3.0, 0.9),
     "wide": (3, 64, 8, 1000, "bf16", 2.5, 0.8),
     "big_vocab": (2, 3, 4, 40000, "bf16", 2.5, 0.8),   # beyond the register-resident row size: streamed passes
+    "big_vocab_f32": (2, 3, 4, 36000, "f32", 2.5, 0.8),  # streamed 16-byte groups of f32 logits
+    "big_vocab_odd": (2, 3, 4, 40003, "bf16", 2.5, 0.8),  # not a multiple of 8: streamed entry by entry
+    "vocab_128k": (1, 4, 3, 128256, "bf16", 3.0, 0.9),    # the 128256-entry vocabulary of the GQA workloads
 }
 
 

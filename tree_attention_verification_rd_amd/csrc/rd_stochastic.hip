@@ -25,7 +25,8 @@
 //                    holds x = t + 1024 j); the sums of the 32 "rows" j come
 //                    from a butterfly reduce-scatter per wave, a scan over
 //                    them picks the row holding the crossing, one block scan
-//                    finds it there.  Longer rows are streamed: each wave
+//                    finds it there.  Longer rows are streamed (16-byte
+//                    loads of 8 entries when V is a multiple of 8): each wave
 //                    takes a contiguous range with coalesced loads;
 //   k_stoch_walk  -- one workgroup per request: the pairs and the request's
 //                    uniforms are staged in LDS; from slot 0, children
@@ -204,6 +205,85 @@ __device__ __forceinline__ void load_row_regs(const StochArgs &a, size_t lrow, f
     }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) qv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, t * 4u, kT * 4 * j, 0));
+}
+
+// Rows whose length is a multiple of 8 are streamed with 16-byte loads:
+// group g holds entries 8g .. 8g+7 (one dwordx4 of bf16 logits or two of
+// f32, two of q).  Offsets past the row read as zero and are masked by the
+// callers.  One wave-wide load then moves 1 KB instead of 128-256 bytes, so a
+// pass over a long row is no longer bound by the rate at which the CU
+// accepts load instructions.
+struct RowRes {
+    rsrc_t l, q;
+};
+__device__ __forceinline__ RowRes row_res(const StochArgs &a, size_t lrow) {
+    const uint32_t V = static_cast<uint32_t>(a.V);
+    RowRes r;
+    r.l = a.is_bf16 ? make_rsrc(static_cast<const uint16_t *>(a.logits) + lrow, V * 2u)
+                    : make_rsrc(static_cast<const float *>(a.logits) + lrow, V * 4u);
+    r.q = make_rsrc(a.q + lrow, V * 4u);
+    return r;
+}
+struct Grp {
+    u32x4 l0, l1, q0, q1;
+};
+__device__ __forceinline__ Grp load_grp(const StochArgs &a, const RowRes &r, uint32_t g, bool with_q) {
+    Grp v;
+    if (a.is_bf16) {
+        v.l0 = __builtin_amdgcn_raw_buffer_load_b128(r.l, g * 16u, 0, 0);
+        v.l1 = u32x4{0, 0, 0, 0};
+    } else {
+        v.l0 = __builtin_amdgcn_raw_buffer_load_b128(r.l, g * 32u, 0, 0);
+        v.l1 = __builtin_amdgcn_raw_buffer_load_b128(r.l, g * 32u + 16u, 0, 0);
+    }
+    if (with_q) {
+        v.q0 = __builtin_amdgcn_raw_buffer_load_b128(r.q, g * 32u, 0, 0);
+        v.q1 = __builtin_amdgcn_raw_buffer_load_b128(r.q, g * 32u + 16u, 0, 0);
+    } else {
+        v.q0 = v.q1 = u32x4{0, 0, 0, 0};
+    }
+    return v;
+}
+// entries of a loaded group as floats, in index order
+__device__ __forceinline__ void unpack_grp(const StochArgs &a, const Grp &v, float (&l)[8], float (&q)[8]) {
+    if (a.is_bf16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            l[2 * k] = __uint_as_float(v.l0[k] << 16);
+            l[2 * k + 1] = __uint_as_float(v.l0[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            l[k] = __uint_as_float(v.l0[k]);
+            l[4 + k] = __uint_as_float(v.l1[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        q[k] = __uint_as_float(v.q0[k]);
+        q[4 + k] = __uint_as_float(v.q1[k]);
+    }
+}
+
+// Visits the groups g = tid, tid + kT, ... < V/8 in batches of kUBV (loads
+// first), calling f(l[8], q[8]) on each.
+constexpr int kUBV = 4;
+template <typename F>
+__device__ __forceinline__ void row_pass_vec(const StochArgs &a, const RowRes &r, bool with_q, F f) {
+    const uint32_t G = static_cast<uint32_t>(a.V) / 8u;
+    for (uint32_t g0 = threadIdx.x; g0 < G; g0 += kT * kUBV) {
+        Grp v[kUBV];
+#pragma unroll
+        for (int j = 0; j < kUBV; ++j) v[j] = load_grp(a, r, g0 + j * kT, with_q);
+#pragma unroll
+        for (int j = 0; j < kUBV; ++j)
+            if (g0 + j * kT < G) {
+                float l[8], q[8];
+                unpack_grp(a, v[j], l, q);
+                f(l, q);
+            }
+    }
 }
 
 // parent slot of every slot of request b (-1 for roots), into LDS
@@ -407,11 +487,126 @@ __device__ __forceinline__ int bonus_streamed(const StochArgs &a, size_t lrow, c
     return first < V ? first : last;
 }
 
+// bonus_streamed on a row of V % 8 == 0 entries with 16-byte loads: wave wv
+// owns groups [wv*GW, (wv+1)*GW), 64 groups (512 entries) a step, lane l
+// holding the 8 consecutive entries of group l of the step.  The crossing is
+// found by a wave scan of the lanes' sums and then inside the lane; when
+// rounding between the levels hides it there, the lane's last entry of
+// nonzero weight stands in.  Result valid in every thread.
+__device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowRes &r, float M, float invS, float c,
+                                                  float u_b, float *red, int *redi) {
+    const int V = a.V;
+    const int G = V / 8;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int GW = (G + kNW - 1) / kNW;
+    const int g0 = min(wv * GW, G), g1 = min(g0 + GW, G);
+    const int nsteps = (g1 - g0 + 63) / 64;
+    constexpr int kSB = 4;  // steps loaded together
+    auto weights = [&](const Grp &v, bool ok, float (&w)[8]) {
+        float l[8], q[8];
+        unpack_grp(a, v, l, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = ok ? fmaxf(__expf(l[e] - M) * invS - c * q[e], 0.f) : 0.f;
+    };
+    float lsum = 0.f;
+    int lastnz = -1;
+    for (int s0 = 0; s0 < nsteps; s0 += kSB) {
+        Grp v[kSB];
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + (s0 + j) * 64 + lane), true);
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+            const int g = g0 + (s0 + j) * 64 + lane;
+            float w[8];
+            weights(v[j], g < g1, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lsum += w[e];
+                if (w[e] > 0.f) lastnz = 8 * g + e;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        lsum += shfl_xor(lsum, off);  // the wave's total, in every lane
+        lastnz = max(lastnz, shfl_xor(lastnz, off));
+    }
+    __syncthreads();
+    if (lane == 0) {
+        red[wv] = lsum;
+        redi[kNW + wv] = lastnz;
+    }
+    __syncthreads();
+    float exc = 0.f, total = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+        if (w2 < wv) exc += red[w2];
+        total += red[w2];
+    }
+    const float thr = u_b * total;
+    int cand = V;
+    if (g0 < g1) {
+        if (exc > thr) {
+            cand = 8 * g0;
+        } else {
+            float carry = exc;
+            for (int s0 = 0; s0 < nsteps && cand == V; s0 += kSB) {
+                Grp v[kSB];
+#pragma unroll
+                for (int j = 0; j < kSB; ++j)
+                    v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + (s0 + j) * 64 + lane), true);
+#pragma unroll
+                for (int j = 0; j < kSB; ++j) {
+                    const int g = g0 + (s0 + j) * 64 + lane;
+                    float w[8];
+                    weights(v[j], g < g1, w);
+                    float tl = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tl += w[e];
+                    float inc = tl;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float o = __shfl_up(inc, off, 64);
+                        if (lane >= off) inc += o;
+                    }
+                    const float tot = __shfl(inc, 63, 64);
+                    const uint64_t hit = __ballot(carry + inc > thr && g < g1);
+                    if (cand == V && hit) {
+                        const int hl = __ffsll(static_cast<long long>(hit)) - 1;
+                        // inside the lane: the first entry whose running sum crosses
+                        float run = carry + (inc - tl);
+                        int es = -1, enz = 7;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            run += w[e];
+                            if (es < 0 && run > thr) es = e;
+                            if (w[e] > 0.f) enz = e;
+                        }
+                        const int eh = __shfl(es >= 0 ? es : enz, hl, 64);
+                        cand = 8 * (g0 + (s0 + j) * 64 + hl) + eh;
+                    }
+                    carry += tot;
+                }
+            }
+        }
+    }
+    if (lane == 0) redi[wv] = cand;
+    __syncthreads();
+    int first = V, last = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+        first = min(first, redi[w2]);
+        last = max(last, redi[kNW + w2]);
+    }
+    return first < V ? first : last;
+}
+
 // Every statistic of one slot: (max, 1/sum) of its logits, the residual
 // sequence (c_i, D_i) for i up to its child count, each child's test pair
 // and the slot's bonus.  With RJ > 0 (V <= kT * RJ) the slot's logits and q
 // are loaded once into registers (element x = tid + kT*j) and every pass runs
-// on them; with RJ == 0 each pass streams the row.
+// on them; with RJ == 0 each pass streams the row entry by entry, with
+// RJ < 0 (V a multiple of 8) in 16-byte groups of 8 entries.
 template <int RJ>
 __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     __shared__ int parent[kMaxSlots];
@@ -433,6 +628,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     const size_t ubase = static_cast<size_t>(b) * P;
     const size_t lrow = (ubase + u) * static_cast<size_t>(V);
     const float *qrow = a.q + lrow;
+    const RowRes rr = row_res(a, lrow);
     float pv[RJ > 0 ? RJ : 1], qv[RJ > 0 ? RJ : 1];  // logits, then p0, and q of this thread's elements
     if constexpr (RJ > 0) load_row_regs<RJ>(a, lrow, pv, qv);  // issued first: the loads overlap the tree build
     if (static_cast<int>(threadIdx.x) < n) tok_sh[threadIdx.x] = a.ptok[ubase + threadIdx.x];
@@ -469,6 +665,23 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
         invS = 1.f / block_sum(s, red);
 #pragma unroll
         for (int j = 0; j < RJ; ++j) pv[j] *= invS;
+    } else if constexpr (RJ < 0) {
+        // one rescale per group of 8: its max first, then the 8 exponentials
+        float m = -INFINITY, s = 0.f;
+        row_pass_vec(a, rr, false, [&](const float (&l)[8], const float (&)[8]) {
+            float gm = l[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) gm = fmaxf(gm, l[e]);
+            const float mn = fmaxf(m, gm);
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += __expf(l[e] - mn);
+            s = s * merge_scale(m, mn) + t;
+            m = mn;
+        });
+        float S;
+        M = block_softmax_stats(m, s, red, &S);
+        invS = 1.f / S;
     } else {
         float m = -INFINITY, s = 0.f;
         row_pass(a, lrow, nullptr, V, [&](int, float l, float) {
@@ -488,6 +701,11 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
         if constexpr (RJ > 0) {
 #pragma unroll
             for (int j = 0; j < RJ; ++j) t += fmaxf(pv[j] - cn * qv[j], 0.f);
+        } else if constexpr (RJ < 0) {
+            row_pass_vec(a, rr, true, [&](const float (&l)[8], const float (&q1)[8]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t += fmaxf(__expf(l[e] - M) * invS - cn * q1[e], 0.f);
+            });
         } else {
             row_pass(a, lrow, qrow, V,
                      [&](int, float l, float q1) { t += fmaxf(__expf(l - M) * invS - cn * q1, 0.f); });
@@ -509,6 +727,8 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     int bonus;
     if constexpr (RJ > 0)
         bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, rows, sh_f, sh_i);
+    else if constexpr (RJ < 0)
+        bonus = bonus_streamed_vec(a, rr, M, invS, c, ub, red, redi);
     else
         bonus = bonus_streamed(a, lrow, qrow, M, invS, c, ub, red, redi);
     if (threadIdx.x == 0) a.bonus[ubase + u] = min(bonus, V - 1);
@@ -594,6 +814,8 @@ hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const in
     const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * W * L));
     if (V <= kT * 32)
         hipLaunchKernelGGL(k_stoch_node<32>, grid, dim3(kT), 0, stream, a);
+    else if (V % 8 == 0)
+        hipLaunchKernelGGL(k_stoch_node<-1>, grid, dim3(kT), 0, stream, a);
     else
         hipLaunchKernelGGL(k_stoch_node<0>, grid, dim3(kT), 0, stream, a);
     hipError_t e = hipGetLastError();
