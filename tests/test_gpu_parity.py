@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import tree_attention_verification_rd_amd as rd
-from synthetic import get_config, draw_beams, base_seed, Config
-from harness import Problem, TOL, normwise_rows, to_np, mask_words_np, fmt_err
+from synthetic import get_config, draw_beams, base_seed, Config, round_to_bf16
+from harness import Problem, TOL, MARGIN, normwise_rows, to_np, mask_words_np, fmt_err
 
 pytestmark = pytest.mark.gpu
 
@@ -235,6 +235,57 @@ def test_lm_head_small(name):
     errs = np.concatenate(errs)
     say(f"    logits normwise error {fmt_err(errs)}")
     assert errs.max() <= TOL[cfg.dtype]
+
+
+# Inner sizes that are not multiples of the k-step: a partial last k-step
+# (K % 64 != 0) and an odd k-step count (the kernel pads with one all-zero
+# step) in both tile shapes -- up to 512 padded rows (the wave-specialized
+# shape) and above.  Packed lengths include 0 and P_max.
+LM_K = {
+    "few_rows_odd_ksteps": (3, 40, 576, 1000),
+    "few_rows_partial_kstep": (3, 40, 584, 1000),
+    "many_rows_odd_ksteps": (4, 160, 520, 777),
+    "many_rows_partial_kstep": (4, 160, 584, 777),
+}
+
+
+@pytest.mark.parametrize("name", list(LM_K))
+def test_lm_head_inner_sizes(name):
+    B, P, K, V = LM_K[name]
+    rng = np.random.default_rng(7100 + list(LM_K).index(name))
+    plen = np.array([P, 0] + list(rng.integers(1, P, size=B - 2)), dtype=np.int32)
+    hidden = round_to_bf16(rng.standard_normal((B, P, K)).astype(np.float32))
+    weight = round_to_bf16((rng.standard_normal((V, K)) * 0.02).astype(np.float32))
+    # redraw valid rows whose fp64 top-1 / top-2 gap is below the margin
+    for _ in range(50):
+        bad = []
+        for b in range(B):
+            lg = oracle.lm_head_logits(hidden[b, :plen[b]], weight)
+            part = np.partition(lg, -2, axis=-1)
+            bad += [(b, p) for p in np.nonzero(part[:, -1] - part[:, -2] < MARGIN)[0]]
+        if not bad:
+            break
+        for b, p in bad:
+            hidden[b, p] = round_to_bf16(rng.standard_normal(K).astype(np.float32))
+    assert not bad
+    say(f"[lm] {name}: B={B} P_max={P} K={K} V={V} rows={int(plen.sum())}")
+    logits, am = rd.rd_lm_head_argmax(torch.from_numpy(hidden).cuda().to(torch.bfloat16),
+                                      torch.from_numpy(plen).cuda(),
+                                      torch.from_numpy(weight).cuda().to(torch.bfloat16))
+    torch.cuda.synchronize()
+    am_np = am.cpu().numpy()
+    lg_np = to_np(logits)
+    errs = []
+    for b in range(B):
+        n = int(plen[b])
+        ref = oracle.lm_head_logits(hidden[b, :n], weight)
+        np.testing.assert_array_equal(am_np[b, :n], oracle.argmax_first(ref), err_msg=f"b={b}")
+        assert (am_np[b, n:] == -1).all()
+        if n:
+            errs.append(normwise_rows(lg_np[b, :n], ref).ravel())
+    errs = np.concatenate(errs)
+    say(f"    logits normwise error {fmt_err(errs)}")
+    assert errs.max() <= TOL["bf16"]
 
 
 # ------------------------------------------------------------- whole step
