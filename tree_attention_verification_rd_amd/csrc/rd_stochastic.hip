@@ -25,9 +25,13 @@
 //                    holds x = t + 1024 j); the sums of the 32 "rows" j come
 //                    from a butterfly reduce-scatter per wave, a scan over
 //                    them picks the row holding the crossing, one block scan
-//                    finds it there.  Longer rows are streamed (16-byte
-//                    loads of 8 entries when V is a multiple of 8): each wave
-//                    takes a contiguous range with coalesced loads;
+//                    finds it there.  Longer rows are streamed.  When V is
+//                    a multiple of 8, every pass reads 16-byte groups of 8
+//                    entries over one contiguous range per wave, so each
+//                    pass also gives per-wave weight sums; the bonus then
+//                    rescans only the range that holds the crossing.
+//                    Otherwise entry by entry, each wave taking a contiguous
+//                    range for the bonus;
 //   k_stoch_walk  -- one workgroup per request: the pairs and the request's
 //                    uniforms are staged in LDS; from slot 0, children
 //                    (slots whose parent is the node, all above it) are
@@ -266,19 +270,26 @@ __device__ __forceinline__ void unpack_grp(const StochArgs &a, const Grp &v, flo
     }
 }
 
-// Visits the groups g = tid, tid + kT, ... < V/8 in batches of kUBV (loads
-// first), calling f(l[8], q[8]) on each.
-constexpr int kUBV = 4;
+// Groups of a row are split into kNW contiguous ranges, one per wavefront
+// (the same ranges in every pass, so each pass also yields per-wavefront
+// sums).  A wavefront walks its range 64 groups (1 KB of bf16 logits) a
+// step, kSBV steps loaded together, calling f(l[8], q[8]) on each group.
+constexpr int kSBV = 4;
+__device__ __forceinline__ void wave_range(int G, int &g0, int &g1) {
+    const int GW = (G + kNW - 1) / kNW;
+    g0 = min(static_cast<int>(threadIdx.x >> 6) * GW, G);
+    g1 = min(g0 + GW, G);
+}
 template <typename F>
-__device__ __forceinline__ void row_pass_vec(const StochArgs &a, const RowRes &r, bool with_q, F f) {
-    const uint32_t G = static_cast<uint32_t>(a.V) / 8u;
-    for (uint32_t g0 = threadIdx.x; g0 < G; g0 += kT * kUBV) {
-        Grp v[kUBV];
+__device__ __forceinline__ void wave_pass(const StochArgs &a, const RowRes &r, bool with_q, int g0, int g1, F f) {
+    const int lane = threadIdx.x & 63;
+    for (int s0 = 0; s0 < g1 - g0; s0 += 64 * kSBV) {
+        Grp v[kSBV];
 #pragma unroll
-        for (int j = 0; j < kUBV; ++j) v[j] = load_grp(a, r, g0 + j * kT, with_q);
+        for (int j = 0; j < kSBV; ++j) v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + s0 + 64 * j + lane), with_q);
 #pragma unroll
-        for (int j = 0; j < kUBV; ++j)
-            if (g0 + j * kT < G) {
+        for (int j = 0; j < kSBV; ++j)
+            if (g0 + s0 + 64 * j + lane < g1) {
                 float l[8], q[8];
                 unpack_grp(a, v[j], l, q);
                 f(l, q);
@@ -487,118 +498,91 @@ __device__ __forceinline__ int bonus_streamed(const StochArgs &a, size_t lrow, c
     return first < V ? first : last;
 }
 
-// bonus_streamed on a row of V % 8 == 0 entries with 16-byte loads: wave wv
-// owns groups [wv*GW, (wv+1)*GW), 64 groups (512 entries) a step, lane l
-// holding the 8 consecutive entries of group l of the step.  The crossing is
-// found by a wave scan of the lanes' sums and then inside the lane; when
-// rounding between the levels hides it there, the lane's last entry of
-// nonzero weight stands in.  Result valid in every thread.
+// Bonus of a row of V % 8 == 0 entries streamed in wavefront ranges.
+// wtot[w] holds the sum of the weights w(x) = max(p0(x) - c q(x), 0) over
+// wavefront w's range, from the pass that last set c.  The crossing lies in
+// the first range whose running total exceeds u_b times the whole (with
+// none, from rounding, the last range of nonzero total), and only that
+// range is scanned: lane sums scanned across the wavefront, then the 8
+// entries of the crossing lane.  Where rounding between the levels hides
+// the crossing, the range's last entry of nonzero weight stands in.  Result
+// valid in every thread.
 __device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowRes &r, float M, float invS, float c,
-                                                  float u_b, float *red, int *redi) {
+                                                  float u_b, const float *wtot, int *redi) {
     const int V = a.V;
     const int G = V / 8;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int GW = (G + kNW - 1) / kNW;
-    const int g0 = min(wv * GW, G), g1 = min(g0 + GW, G);
-    const int nsteps = (g1 - g0 + 63) / 64;
-    constexpr int kSB = 4;  // steps loaded together
-    auto weights = [&](const Grp &v, bool ok, float (&w)[8]) {
-        float l[8], q[8];
-        unpack_grp(a, v, l, q);
+    float total = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = ok ? fmaxf(__expf(l[e] - M) * invS - c * q[e], 0.f) : 0.f;
-    };
-    float lsum = 0.f;
-    int lastnz = -1;
-    for (int s0 = 0; s0 < nsteps; s0 += kSB) {
-        Grp v[kSB];
-#pragma unroll
-        for (int j = 0; j < kSB; ++j) v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + (s0 + j) * 64 + lane), true);
-#pragma unroll
-        for (int j = 0; j < kSB; ++j) {
-            const int g = g0 + (s0 + j) * 64 + lane;
-            float w[8];
-            weights(v[j], g < g1, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lsum += w[e];
-                if (w[e] > 0.f) lastnz = 8 * g + e;
-            }
-        }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        lsum += shfl_xor(lsum, off);  // the wave's total, in every lane
-        lastnz = max(lastnz, shfl_xor(lastnz, off));
-    }
-    __syncthreads();
-    if (lane == 0) {
-        red[wv] = lsum;
-        redi[kNW + wv] = lastnz;
-    }
-    __syncthreads();
-    float exc = 0.f, total = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) {
-        if (w2 < wv) exc += red[w2];
-        total += red[w2];
-    }
+    for (int w2 = 0; w2 < kNW; ++w2) total += wtot[w2];
     const float thr = u_b * total;
-    int cand = V;
-    if (g0 < g1) {
-        if (exc > thr) {
-            cand = 8 * g0;
-        } else {
-            float carry = exc;
-            for (int s0 = 0; s0 < nsteps && cand == V; s0 += kSB) {
-                Grp v[kSB];
-#pragma unroll
-                for (int j = 0; j < kSB; ++j)
-                    v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + (s0 + j) * 64 + lane), true);
-#pragma unroll
-                for (int j = 0; j < kSB; ++j) {
-                    const int g = g0 + (s0 + j) * 64 + lane;
-                    float w[8];
-                    weights(v[j], g < g1, w);
-                    float tl = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) tl += w[e];
-                    float inc = tl;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float o = __shfl_up(inc, off, 64);
-                        if (lane >= off) inc += o;
-                    }
-                    const float tot = __shfl(inc, 63, 64);
-                    const uint64_t hit = __ballot(carry + inc > thr && g < g1);
-                    if (cand == V && hit) {
-                        const int hl = __ffsll(static_cast<long long>(hit)) - 1;
-                        // inside the lane: the first entry whose running sum crosses
-                        float run = carry + (inc - tl);
-                        int es = -1, enz = 7;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            run += w[e];
-                            if (es < 0 && run > thr) es = e;
-                            if (w[e] > 0.f) enz = e;
-                        }
-                        const int eh = __shfl(es >= 0 ? es : enz, hl, 64);
-                        cand = 8 * (g0 + (s0 + j) * 64 + hl) + eh;
-                    }
-                    carry += tot;
-                }
-            }
-        }
-    }
-    if (lane == 0) redi[wv] = cand;
-    __syncthreads();
-    int first = V, last = 0;
+    int ws = -1, wlast = -1;
+    float exc = 0.f, ews = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kNW; ++w2) {
-        first = min(first, redi[w2]);
-        last = max(last, redi[kNW + w2]);
+        if (ws < 0 && exc + wtot[w2] > thr) {
+            ws = w2;
+            ews = exc;
+        }
+        if (wtot[w2] > 0.f) wlast = w2;
+        exc += wtot[w2];
     }
-    return first < V ? first : last;
+    if (ws < 0) {  // rounding put the threshold at or past the total
+        ws = wlast >= 0 ? wlast : kNW - 1;
+        ews = -INFINITY;  // never crosses: the range's last nonzero entry stands in
+    }
+    if (wv == ws) {
+        int g0, g1;
+        wave_range(G, g0, g1);
+        int cand = -1, lastnz = -1;
+        float carry = ews;
+        for (int s0 = 0; s0 < g1 - g0 && cand < 0; s0 += 64 * kSBV) {
+            Grp v[kSBV];
+#pragma unroll
+            for (int j = 0; j < kSBV; ++j)
+                v[j] = load_grp(a, r, static_cast<uint32_t>(g0 + s0 + 64 * j + lane), true);
+#pragma unroll
+            for (int j = 0; j < kSBV; ++j) {
+                const int g = g0 + s0 + 64 * j + lane;
+                float l[8], q[8], w[8];
+                unpack_grp(a, v[j], l, q);
+                float tl = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    w[e] = g < g1 ? fmaxf(__expf(l[e] - M) * invS - c * q[e], 0.f) : 0.f;
+                    tl += w[e];
+                    if (w[e] > 0.f) lastnz = 8 * g + e;
+                }
+                float inc = tl;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_up(inc, off, 64);
+                    if (lane >= off) inc += o;
+                }
+                const float tot = __shfl(inc, 63, 64);
+                const uint64_t hit = __ballot(carry + inc > thr && g < g1);
+                if (cand < 0 && hit) {
+                    const int hl = __ffsll(static_cast<long long>(hit)) - 1;
+                    float run = carry + (inc - tl);
+                    int es = -1, enz = 7;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        run += w[e];
+                        if (es < 0 && run > thr) es = e;
+                        if (w[e] > 0.f) enz = e;
+                    }
+                    const int eh = __shfl(es >= 0 ? es : enz, hl, 64);
+                    cand = 8 * (g0 + s0 + 64 * j + hl) + eh;
+                }
+                carry += tot;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) lastnz = max(lastnz, shfl_xor(lastnz, off));
+        if (lane == 0) redi[0] = cand >= 0 ? cand : max(lastnz, 0);
+    }
+    __syncthreads();
+    return redi[0];
 }
 
 // Every statistic of one slot: (max, 1/sum) of its logits, the residual
@@ -619,6 +603,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     __shared__ float sh_f[2];
     __shared__ int sh_i[2];
     __shared__ int nkids_sh;
+    __shared__ float wtot[kNW];  // streamed rows: per-wavefront weight sums for the bonus
     const int W = a.W, L = a.L, V = a.V;
     const int P = W * L;
     const int b = blockIdx.x / P;
@@ -629,6 +614,8 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     const size_t lrow = (ubase + u) * static_cast<size_t>(V);
     const float *qrow = a.q + lrow;
     const RowRes rr = row_res(a, lrow);
+    int vg0 = 0, vg1 = 0;  // this wavefront's range of 8-entry groups (streamed rows)
+    if constexpr (RJ < 0) wave_range(V / 8, vg0, vg1);
     float pv[RJ > 0 ? RJ : 1], qv[RJ > 0 ? RJ : 1];  // logits, then p0, and q of this thread's elements
     if constexpr (RJ > 0) load_row_regs<RJ>(a, lrow, pv, qv);  // issued first: the loads overlap the tree build
     if (static_cast<int>(threadIdx.x) < n) tok_sh[threadIdx.x] = a.ptok[ubase + threadIdx.x];
@@ -668,7 +655,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     } else if constexpr (RJ < 0) {
         // one rescale per group of 8: its max first, then the 8 exponentials
         float m = -INFINITY, s = 0.f;
-        row_pass_vec(a, rr, false, [&](const float (&l)[8], const float (&)[8]) {
+        wave_pass(a, rr, false, vg0, vg1, [&](const float (&l)[8], const float (&)[8]) {
             float gm = l[0];
 #pragma unroll
             for (int e = 1; e < 8; ++e) gm = fmaxf(gm, l[e]);
@@ -682,6 +669,10 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
         float S;
         M = block_softmax_stats(m, s, red, &S);
         invS = 1.f / S;
+        // red holds each wavefront's merged (max, sum): its range's share of
+        // p0, the bonus weights while c = 0
+        if (static_cast<int>(threadIdx.x) < kNW)
+            wtot[threadIdx.x] = red[kNW + threadIdx.x] * merge_scale(red[threadIdx.x], M) * invS;
     } else {
         float m = -INFINITY, s = 0.f;
         row_pass(a, lrow, nullptr, V, [&](int, float l, float) {
@@ -702,7 +693,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
 #pragma unroll
             for (int j = 0; j < RJ; ++j) t += fmaxf(pv[j] - cn * qv[j], 0.f);
         } else if constexpr (RJ < 0) {
-            row_pass_vec(a, rr, true, [&](const float (&l)[8], const float (&q1)[8]) {
+            wave_pass(a, rr, true, vg0, vg1, [&](const float (&l)[8], const float (&q1)[8]) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) t += fmaxf(__expf(l[e] - M) * invS - cn * q1[e], 0.f);
             });
@@ -714,6 +705,8 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
         if (T > 0.f) {
             c = cn;
             D = T;
+            // red holds the wavefronts' sums of max(p0 - c q, 0) for the new c
+            if (RJ < 0 && static_cast<int>(threadIdx.x) < kNW) wtot[threadIdx.x] = red[threadIdx.x];
         }
         if (threadIdx.x == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
     }
@@ -728,7 +721,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     if constexpr (RJ > 0)
         bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, rows, sh_f, sh_i);
     else if constexpr (RJ < 0)
-        bonus = bonus_streamed_vec(a, rr, M, invS, c, ub, red, redi);
+        bonus = bonus_streamed_vec(a, rr, M, invS, c, ub, wtot, redi);
     else
         bonus = bonus_streamed(a, lrow, qrow, M, invS, c, ub, red, redi);
     if (threadIdx.x == 0) a.bonus[ubase + u] = min(bonus, V - 1);
