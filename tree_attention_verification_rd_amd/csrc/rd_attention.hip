@@ -298,23 +298,39 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         const int lim = cache ? nck : tok_hi - (i - ncache) * kBlockN;
         const bool full = cache && ic * kblk + kmul * (kBlockN - 1) < nck;  // wave-uniform
         const int wi = 2 * (i - ncache);
-        if (!full) {
+        if (!full && cache) {
+            // partial cache tile: key j is valid iff its position is below lim
 #pragma unroll
-            for (int qi = 0; qi < NQ; ++qi) {
-                uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
-                if (!cache) {
-                    w0 = mwords[lt[qi] * a.nw + wi];
-                    w1 = (wi + 1 < a.nw) ? mwords[lt[qi] * a.nw + wi + 1] : 0u;
-                }
+            for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = (wk * NKB + kb) * 16 + 4 * kg + e;
-                        const uint32_t wd = (j < 32) ? w0 : w1;
-                        const bool vis = cache ? (ic * kblk + kmul * j < lim) : ((j < lim) && ((wd >> (j & 31)) & 1u));
+                        sc[qi][kb][e] = (ic * kblk + kmul * j < lim) ? sc[qi][kb][e] : -INFINITY;
+                    }
+        } else if (!full) {
+            // packed tile: key j = jj + 4*kg (jj = (wk*NKB + kb)*16 + e) is
+            // visible iff j < lim and bit j of the row's mask words is set.
+            // j stays in jj's 16-key block, so its word is chosen by jj and its
+            // bit is bit (jj & 31) of the word shifted right by 4*kg once.
+            const int lim2 = lim - 4 * kg;
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                const uint32_t w0 = mwords[lt[qi] * a.nw + wi];
+                const uint32_t w1 = (wi + 1 < a.nw) ? mwords[lt[qi] * a.nw + wi + 1] : 0u;
+                const uint32_t s0 = w0 >> (4 * kg), s1 = w1 >> (4 * kg);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int jb = (wk * NKB + kb) * 16;  // wave-uniform
+                    const uint32_t sw = (jb < 32) ? s0 : s1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = jb + e;
+                        const bool vis = (jj < lim2) && ((sw >> ((kb * 16 + e) & 31)) & 1u);
                         sc[qi][kb][e] = vis ? sc[qi][kb][e] : -INFINITY;
                     }
+                }
             }
         }
         bf16x8 pb[NQ][NKS];
