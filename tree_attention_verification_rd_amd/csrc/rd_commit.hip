@@ -42,7 +42,7 @@ __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
     const int c = a.kv_len[b];
     const bool ok = w >= 0 && w < a.W && n >= 0 && n < a.L && c >= 0 && c <= a.S - (n + 1);
     const int rows = n + 1;
-    if (ok && threadIdx.x < rows) {
+    if (ok && static_cast<int>(threadIdx.x) < rows) {
         const int s = a.unpacker[(static_cast<size_t>(b) * a.W + w) * a.L + threadIdx.x];
         slot[threadIdx.x] = min(max(s, 0), a.P - 1);
     }

@@ -42,12 +42,6 @@ struct LmArgs {
     int nvt, nrt;
 };
 
-__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-    bf16x8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
@@ -475,7 +469,7 @@ __global__ __launch_bounds__(256) void k_lm_head_f32(const float *__restrict__ h
     ri[threadIdx.x] = (v < V) ? v : 0x7fffffff;
     __syncthreads();
     for (int off = 128; off > 0; off >>= 1) {
-        if (threadIdx.x < off &&
+        if (static_cast<int>(threadIdx.x) < off &&
             better(rv[threadIdx.x + off], ri[threadIdx.x + off], rv[threadIdx.x], ri[threadIdx.x])) {
             rv[threadIdx.x] = rv[threadIdx.x + off];
             ri[threadIdx.x] = ri[threadIdx.x + off];
