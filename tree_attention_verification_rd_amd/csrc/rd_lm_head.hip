@@ -104,10 +104,14 @@ __device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32
 // memory pipeline full) then holds up only its own wavefront, while the
 // SIMD's multiplying wavefront keeps the MFMA pipe fed.  Needs a wave tile
 // that fits 256 registers.
-template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK, bool KROT, bool SPEC>
-__global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) {
-    constexpr int NT = SPEC ? 512 : 256;
-    static_assert(GV * GR == 4, "four wavefronts per workgroup");
+// NWV: wavefronts that both load and multiply (4, or 8 for two per SIMD;
+// with SPEC four of each kind).
+template <int WV, int WR, int GV, int GR, int NSW, int NSX, int BK, bool KROT, bool SPEC, int NWV = 4>
+__global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArgs a) {
+    constexpr int NCW = SPEC ? 4 : NWV;  // multiplying wavefronts
+    constexpr int NLD = SPEC ? 4 : NWV;  // loading wavefronts
+    constexpr int NT = SPEC ? 512 : 64 * NWV;
+    static_assert(GV * GR == NCW, "one wave tile per multiplying wavefront");
     static_assert(NSX >= 2 && NSW >= NSX, "each ring needs a stage in flight while another is consumed");
     static_assert(BK == 32 || BK == 64, "one or two 32-wide MFMA steps per k-step");
     constexpr int NSUB = BK / 32;            // MFMA k-steps per staged k-step
@@ -121,10 +125,10 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
     constexpr int kWStage = BV * kRowB;      // bytes of one weight stage
     constexpr int kXStage = BR * kRowB;      // bytes of one hidden stage
     constexpr int kXBase = NSW * kWStage;    // hidden ring after the weight ring
-    constexpr int NL = (BV + BR) / RPL / 4;  // LDS loads per wavefront per k-step (both operands)
-    constexpr int NLW = BV / RPL / 4;        // ... of weight rows
-    constexpr int NLX = BR / RPL / 4;        // ... of hidden rows
-    static_assert(BV % (4 * RPL) == 0 && BR % (4 * RPL) == 0, "each wavefront loads whole groups of both operands");
+    constexpr int NL = (BV + BR) / RPL / NLD;  // LDS loads per loading wavefront per k-step (both operands)
+    constexpr int NLW = BV / RPL / NLD;        // ... of weight rows
+    constexpr int NLX = BR / RPL / NLD;        // ... of hidden rows
+    static_assert(BV % (NLD * RPL) == 0 && BR % (NLD * RPL) == 0, "each wavefront loads whole groups of both operands");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NSW * kWStage + NSX * kXStage];
     __shared__ int32_t rmap[BR];  // packed row (b*P + p) of each compact row of the tile
     __shared__ int scan_tmp[NT / 64];
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
     const int kg = lane >> 4;
     const bool loader = SPEC && wave >= 4;   // issues loads only
     const bool issues = !SPEC || loader;     // issues ring loads
-    const int cw = wave & 3;                 // index among the multiplying wavefronts
-    const int lw = wave & 3;                 // index among the loading wavefronts
+    const int cw = SPEC ? (wave & 3) : wave;  // index among the multiplying wavefronts
+    const int lw = SPEC ? (wave & 3) : wave;  // index among the loading wavefronts
     const int gv = cw % GV;
     const int gr = cw / GV;
     const int K = a.K;
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
         uint32_t xbase[NLX];
 #pragma unroll
         for (int i = 0; i < NLX; ++i) {
-            const int m = r0 + RPL * (4 * i + lw) + lrow;
+            const int m = r0 + RPL * (NLD * i + lw) + lrow;
             xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
         }
         // The weight rows of k-step kt (k-step (kt + krot) mod nk) go to
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
             const uint32_t sbase = lds0 + slot * kWStage + lw * 1024;
 #pragma unroll
             for (int i = 0; i < NLW; ++i)
-                lds_dma16(sbase + i * 4096, wres, kin ? wbase + i * 4 * RPL * rowb + kadd : kOOB);
+                lds_dma16(sbase + i * NLD * 1024, wres, kin ? wbase + i * NLD * RPL * rowb + kadd : kOOB);
         };
         auto issue_x = [&](int kt, int slot) {
             const int kr = kstep_of(kt);
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
             const uint32_t sbase = lds0 + kXBase + slot * kXStage + lw * 1024;
 #pragma unroll
             for (int i = 0; i < NLX; ++i)
-                lds_dma16(sbase + i * 4096, xres, kin ? xbase[i] + kadd : kOOB);
+                lds_dma16(sbase + i * NLD * 1024, xres, kin ? xbase[i] + kadd : kOOB);
         };
         // a wavefront whose rows are all padding only helps with the loads
         const bool active = !loader && r0 + gr * WR < R;
@@ -306,9 +310,9 @@ __global__ __launch_bounds__(SPEC ? 512 : 256, 1) void k_lm_head_bf16(LmArgs a) 
             const uint32_t sbx = lds0 + kXBase + xsl * kXStage + lw * 1024;
             auto issue_one = [&](int j) {
                 if (j < NLW)
-                    lds_dma16(sbw + j * 4096, wres, kinw ? wbase + j * 4 * RPL * rowb + kaddw : kOOB);
+                    lds_dma16(sbw + j * NLD * 1024, wres, kinw ? wbase + j * NLD * RPL * rowb + kaddw : kOOB);
                 else
-                    lds_dma16(sbx + (j - NLW) * 4096, xres, kinx ? xbase[j - NLW] + kaddx : kOOB);
+                    lds_dma16(sbx + (j - NLW) * NLD * 1024, xres, kinx ? xbase[j - NLW] + kaddx : kOOB);
             };
             if (active) {
                 const uint8_t *wst = lds + wslot * kWStage;
@@ -549,11 +553,14 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
         // tiles to spread over the CUs -- with four more wavefronts that only
         // issue the loads (measured at llama_mha size: 77-80 us against 89-94
         // us with one wavefront per SIMD doing both).  Many rows (the MFMAs
-        // dominate): 256 x 256 per tile, 128x128 per wavefront (too many
-        // registers for a second wavefront per SIMD), k-steps of 32, five
-        // weight and four hidden stages -- a third less L2 traffic per flop.
-        // (Ring depths measured on MI355X: deeper weight rings slow the
-        // few-row shape.)
+        // dominate): 256 x 256 per tile -- a third less L2 traffic per flop
+        // -- over eight wavefronts of 128x64 that all load and multiply, two
+        // per SIMD, so one's stalled load issue leaves the MFMA pipe to the
+        // other; k-steps of 64 and two stages of each operand (measured
+        // against four wavefronts of 128x128 with k-steps of 32 and 5 + 4
+        // stages: gqa 1590 vs 1675 us, long_ctx 473 vs 522, dedup_p0.5
+        // 6938 vs 7144).  (Ring depths measured on MI355X: deeper weight
+        // rings slow the few-row shape.)
         // RD_LM_VARIANT forces one.
         const char *env = getenv("RD_LM_VARIANT");
         plan.variant = (env && *env) ? (atoi(env) != 0) : (plan.rows_pad > 512 ? 1 : 0);
@@ -596,7 +603,7 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         if (plan.variant == 0)
             hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 1, 4, 3, 3, 64, true, true>), grid, dim3(512), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_lm_head_bf16<128, 128, 2, 2, 5, 4, 32, true, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_lm_head_bf16<128, 64, 2, 4, 2, 2, 64, true, false, 8>), grid, dim3(512), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
