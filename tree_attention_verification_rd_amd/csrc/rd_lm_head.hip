@@ -13,9 +13,10 @@
 // vocabulary entries of one row -- what the argmax epilogue and the logits
 // store want.  Both operands are staged through LDS by direct global->LDS
 // loads (no registers, whole cache lines per instruction) into a ring of
-// k-steps, and each of the four multiplying wavefronts computes a 128 x WR
-// block out of LDS with v_mfma_f32_16x16x32_bf16 (in the few-row shape four
-// further wavefronts issue the loads).  The epilogue reduces
+// k-steps, and each multiplying wavefront computes a WV x WR block out of
+// LDS with v_mfma_f32_16x16x32_bf16: in the few-row shape four such
+// wavefronts plus four that only issue the loads, in the many-row shape
+// eight that both load and multiply.  The epilogue reduces
 // (max, first index) over the tile's vocabulary range and writes one
 // partial per (row, vocabulary tile); a second kernel reduces the partials
 // in a fixed order.
@@ -159,9 +160,9 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
     // (by row & 7 for 8 chunks, by (row >> 1) & 3 for 4), so the fragment
     // reads below (16 rows x one chunk per instruction) hit distinct banks.
     // Lane i of a load covers staged row RPL*j + i/CPR and stores LDS slot
-    // i % CPR, which holds chunk slot ^ swizzle(row).  Load j = 4*i + wave
-    // is the wavefront's i-th: its first NLW loads are weight rows, the rest
-    // hidden rows.
+    // i % CPR, which holds chunk slot ^ swizzle(row).  Load j = NLD*i + lw
+    // (lw: the index among the NLD loading wavefronts) is that wavefront's
+    // i-th: its first NLW loads are weight rows, the rest hidden rows.
     auto swz = [](int row) { return CPR == 8 ? (row & 7) : ((row >> 1) & 3); };
     const int lrow = lane / CPR;
     const int lchunk = (lane % CPR) ^ swz(lrow);
