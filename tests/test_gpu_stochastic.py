@@ -65,6 +65,7 @@ CASES = {
     "f32": (5, 3, 5, 300, "f32", 1.5, 0.5),
     "llama_vocab": (8, 8, 5, 32000, "bf16", 3.0, 0.9),
     "wide": (3, 64, 8, 1000, "bf16", 2.5, 0.8),
+    "odd_vocab": (4, 4, 4, 1003, "bf16", 2.0, 0.8),      # register-resident rows loaded entry by entry
     "big_vocab": (2, 3, 4, 40000, "bf16", 2.5, 0.8),   # beyond the register-resident row size: streamed passes
     "big_vocab_f32": (2, 3, 4, 36000, "f32", 2.5, 0.8),  # streamed 16-byte groups of f32 logits
     "big_vocab_odd": (2, 3, 4, 40003, "bf16", 2.5, 0.8),  # not a multiple of 8: streamed entry by entry

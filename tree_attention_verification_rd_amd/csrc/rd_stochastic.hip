@@ -22,10 +22,11 @@
 //                    rejected: the first index whose running sum of
 //                    w = max(p0 - c_nk q, 0) exceeds u_bonus times its total.
 //                    Up to 32K entries the row stays in registers (thread t
-//                    holds x = t + 1024 j); the sums of the 32 "rows" j come
-//                    from a butterfly reduce-scatter per wave, a scan over
-//                    them picks the row holding the crossing, one block scan
-//                    finds it there.  Longer rows are streamed.  When V is
+//                    holds groups of 8 consecutive entries x = 8(t + 1024 g)
+//                    + e, g < 4, loaded 16 bytes at a time when V is a
+//                    multiple of 8); the four groups' sums pick the group
+//                    holding the crossing, a block scan of the threads' sums
+//                    there picks the thread, and its 8 entries the index.  Longer rows are streamed.  When V is
 //                    a multiple of 8, every pass reads 16-byte groups of 8
 //                    entries over one contiguous range per wave, so each
 //                    pass also gives per-wave weight sums; the bonus then
@@ -188,27 +189,68 @@ __device__ __forceinline__ void row_pass(const StochArgs &a, size_t lrow, const 
     }
 }
 
-// This thread's elements x = tid + kT*j (j < RJ) of a row, by buffer loads:
-// one address register serves all of them (the step is a scalar offset) and
-// reads past the row's end give zero.
+// This thread's RJ entries of a row: entry j is x = 8*(tid + kT*(j/8)) + j%8,
+// so each group of 8 is consecutive.  When V is a multiple of 8 every group
+// is one 16-byte load of bf16 logits (two of f32) and two of q; otherwise
+// the same entries are loaded one by one.  Reads past the row give zero.
+__device__ __forceinline__ int reg_x(int j) { return 8 * (static_cast<int>(threadIdx.x) + kT * (j >> 3)) + (j & 7); }
 template <int RJ>
 __device__ __forceinline__ void load_row_regs(const StochArgs &a, size_t lrow, float (&lv)[RJ], float (&qv)[RJ]) {
+    static_assert(RJ % 8 == 0, "whole groups of 8 entries");
+    constexpr int RG = RJ / 8;
     const uint32_t V = static_cast<uint32_t>(a.V), t = threadIdx.x;
     const rsrc_t rq = make_rsrc(a.q + lrow, V * 4u);
+    if (V % 8 == 0) {
+        u32x4 l0[RG], l1[RG], q0[RG], q1[RG];
+        if (a.is_bf16) {
+            const rsrc_t rl = make_rsrc(static_cast<const uint16_t *>(a.logits) + lrow, V * 2u);
+#pragma unroll
+            for (int g = 0; g < RG; ++g) l0[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, (t + kT * g) * 16u, 0, 0);
+        } else {
+            const rsrc_t rl = make_rsrc(static_cast<const float *>(a.logits) + lrow, V * 4u);
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                l0[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, (t + kT * g) * 32u, 0, 0);
+                l1[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, (t + kT * g) * 32u + 16u, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            q0[g] = __builtin_amdgcn_raw_buffer_load_b128(rq, (t + kT * g) * 32u, 0, 0);
+            q1[g] = __builtin_amdgcn_raw_buffer_load_b128(rq, (t + kT * g) * 32u + 16u, 0, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (a.is_bf16) {
+                    lv[8 * g + 2 * k] = __uint_as_float(l0[g][k] << 16);
+                    lv[8 * g + 2 * k + 1] = __uint_as_float(l0[g][k] & 0xFFFF0000u);
+                } else {
+                    lv[8 * g + k] = __uint_as_float(l0[g][k]);
+                    lv[8 * g + 4 + k] = __uint_as_float(l1[g][k]);
+                }
+                qv[8 * g + k] = __uint_as_float(q0[g][k]);
+                qv[8 * g + 4 + k] = __uint_as_float(q1[g][k]);
+            }
+        return;
+    }
     if (a.is_bf16) {
         const rsrc_t rl = make_rsrc(static_cast<const uint16_t *>(a.logits) + lrow, V * 2u);
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rl, t * 2u, kT * 2 * j, 0);
+            const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rl, static_cast<uint32_t>(reg_x(j)) * 2u, 0, 0);
             lv[j] = __uint_as_float(h << 16);
         }
     } else {
         const rsrc_t rl = make_rsrc(static_cast<const float *>(a.logits) + lrow, V * 4u);
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, t * 4u, kT * 4 * j, 0));
+        for (int j = 0; j < RJ; ++j)
+            lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, static_cast<uint32_t>(reg_x(j)) * 4u, 0, 0));
     }
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) qv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, t * 4u, kT * 4 * j, 0));
+    for (int j = 0; j < RJ; ++j)
+        qv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, static_cast<uint32_t>(reg_x(j)) * 4u, 0, 0));
 }
 
 // Rows whose length is a multiple of 8 are streamed with 16-byte loads:
@@ -323,88 +365,99 @@ __device__ __forceinline__ int children_of(int u, int n, const int *parent, int 
     return *cnt_sh;
 }
 
-// Bonus of a register-resident row: thread t holds p0 and q of
-// x = t + kT*j in pv[j], qv[j] (zeros past the row), so the weight of x is
-// max(pv[j] - c qv[j], 0).  Returns, in every thread, the first x whose
-// running sum in x order exceeds u_b times the total.  When rounding between
-// the two levels hides the crossing, or u_b * total rounds up to the total,
-// the last index of nonzero weight stands in (where the crossing lies in
-// exact arithmetic).
+// Bonus of a register-resident row: thread t holds p0 and q of its entries
+// x = reg_x(j) in pv[j], qv[j] (zeros past the row), so the weight of x is
+// max(pv[j] - c qv[j], 0).  The row is RJ/8 groups of 8*kT consecutive
+// entries.  The group holding the crossing of u_b times the total is found
+// from the groups' sums, then the thread by a block scan of the threads' sums
+// in that group, then the entry among the thread's 8.  When rounding between
+// the levels hides the crossing, the last entry of nonzero weight of the
+// chosen group (or thread) stands in, where the crossing lies in exact
+// arithmetic.  Returns the index in every thread.
 template <int RJ>
 __device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&qv)[RJ], float c, float u_b,
-                                          float *red, int *redi, float (*rows)[RJ], float *sh_f, int *sh_i) {
-    static_assert(RJ == 32, "the reduce-scatter below halves 32 rows over lane bits 5..1");
+                                          float *red, int *redi, float *gsum) {
+    constexpr int RG = RJ / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    auto wt = [&](int j) { return fmaxf(pv[j] - c * qv[j], 0.f); };
-    // Row sums by reduce-scatter: the step on lane bit m keeps the half of
-    // the rows that bit selects, adding the partner's copy of them; lane l
-    // ends with row l >> 1 of the wave, and a last step adds lanes l, l^1.
-    float h[16];
-    {
-        const bool up = lane & 32;
+    float w[RJ];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const float lo = wt(k), hi = wt(k + 16);
-            h[k] = (up ? hi : lo) + shfl_xor(up ? lo : hi, 32);
-        }
+    for (int j = 0; j < RJ; ++j) w[j] = fmaxf(pv[j] - c * qv[j], 0.f);
+    float ts[RG];  // this thread's sum in each group
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        ts[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ts[g] += w[8 * g + e];
     }
+    // group sums: per wave, then the waves in index order
 #pragma unroll
-    for (int half = 8, m = 16; half >= 1; half >>= 1, m >>= 1) {
-        const bool up = lane & m;
+    for (int g = 0; g < RG; ++g) {
+        float v = ts[g];
 #pragma unroll
-        for (int k = 0; k < half; ++k) h[k] = (up ? h[k + half] : h[k]) + shfl_xor(up ? h[k] : h[k + half], m);
-    }
-    h[0] += shfl_xor(h[0], 1);
-    if (!(lane & 1)) rows[wave][lane >> 1] = h[0];
-    __syncthreads();
-    if (wave == 0) {
-        float R = 0.f;
-        if (lane < RJ)
-            for (int w2 = 0; w2 < kNW; ++w2) R += rows[w2][lane];
-        float I = R;  // inclusive scan of the row sums
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(I, off, 64);
-            if (lane >= off) I += o;
-        }
-        const float up1 = __shfl_up(I, 1, 64);
-        const float E = lane ? up1 : 0.f;
-        const float thr = u_b * __shfl(I, 63, 64);
-        const uint64_t hit = __ballot(lane < RJ && I > thr);
-        const uint64_t nz = __ballot(lane < RJ && R > 0.f);
-        const int js = hit ? __ffsll(static_cast<long long>(hit)) - 1
-                           : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
-        if (lane == js) {
-            sh_i[0] = js;
-            sh_i[1] = hit ? 1 : 0;
-            sh_f[0] = E;
-            sh_f[1] = thr;
-        }
+        for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
+        if (lane == 0) gsum[g * kNW + wave] = v;
     }
     __syncthreads();
-    const int js = sh_i[0];
-    const bool exact = sh_i[1] != 0;
-    const float E = sh_f[0], thr = sh_f[1];
-    float v = 0.f;
+    float S[RG], total = 0.f;
 #pragma unroll
-    for (int j = 0; j < RJ; ++j)
-        if (j == js) v = wt(j);
+    for (int g = 0; g < RG; ++g) {
+        S[g] = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kNW; ++w2) S[g] += gsum[g * kNW + w2];
+        total += S[g];
+    }
+    const float thr = u_b * total;
+    int gs = -1, glast = 0;
+    float E = 0.f, run = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        if (gs < 0 && run + S[g] > thr) {
+            gs = g;
+            E = run;
+        }
+        if (S[g] > 0.f) glast = g;
+        run += S[g];
+    }
+    const bool exact = gs >= 0;
+    if (!exact) gs = glast;
+    float mine = 0.f;  // this thread's sum in the chosen group
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        if (g == gs) mine = ts[g];
     float tot;
-    const float inc = block_scan(v, red, tot);
+    const float inc = block_scan(mine, red, tot);
     const uint64_t hit = __ballot(exact && E + inc > thr);
-    const uint64_t nz = __ballot(v > 0.f);
+    const uint64_t nz = __ballot(mine > 0.f);
     if (lane == 0) {
         redi[wave] = hit ? wave * 64 + __ffsll(static_cast<long long>(hit)) - 1 : kT;
         redi[kNW + wave] = nz ? wave * 64 + 63 - __clzll(static_cast<long long>(nz)) : -1;
     }
     __syncthreads();
-    int first = kT, last = 0;
+    int first = kT, last = -1;
 #pragma unroll
     for (int w2 = 0; w2 < kNW; ++w2) {
         first = min(first, redi[w2]);
         last = max(last, redi[kNW + w2]);
     }
-    return (first < kT ? first : last) + kT * js;
+    const int tsel = first < kT ? first : max(last, 0);
+    // the entry among the chosen thread's 8 (its running sum from E + its exclusive prefix)
+    if (static_cast<int>(threadIdx.x) == tsel) {
+        float r = E + (inc - mine);
+        int es = -1, enz = 0;
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+            if (g == gs) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    r += w[8 * g + e];
+                    if (es < 0 && first < kT && r > thr) es = e;
+                    if (w[8 * g + e] > 0.f) enz = e;
+                }
+            }
+        redi[2 * kNW] = 8 * (tsel + kT * gs) + (es >= 0 ? es : enz);
+    }
+    __syncthreads();
+    return redi[2 * kNW];
 }
 
 // Bonus of a streamed row (p0 = exp(l - M) * invS, weight max(p0 - c q, 0)):
@@ -597,11 +650,9 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     __shared__ int kids[kMaxBeams];
     __shared__ float2 cd_sh[kMaxBeams];
     __shared__ float red[2 * kNW];
-    __shared__ int redi[2 * kNW];
+    __shared__ int redi[2 * kNW + 1];
     __shared__ int tok_sh[kMaxSlots];
-    __shared__ float rows[kNW][RJ > 0 ? RJ : 1];
-    __shared__ float sh_f[2];
-    __shared__ int sh_i[2];
+    __shared__ float gsum[(RJ > 0 ? RJ / 8 : 1) * kNW];
     __shared__ int nkids_sh;
     __shared__ float wtot[kNW];  // streamed rows: per-wavefront weight sums for the bonus
     const int W = a.W, L = a.L, V = a.V;
@@ -639,12 +690,12 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < RJ; ++j)
-            if (static_cast<int>(threadIdx.x) + kT * j < V) m = fmaxf(m, pv[j]);
+            if (reg_x(j) < V) m = fmaxf(m, pv[j]);
         M = block_max(m, red);
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < RJ; ++j) {
-            const bool ok = static_cast<int>(threadIdx.x) + kT * j < V;
+            const bool ok = reg_x(j) < V;
             pv[j] = ok ? __expf(pv[j] - M) : 0.f;
             qv[j] = ok ? qv[j] : 0.f;
             s += pv[j];
@@ -719,7 +770,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     const float ub = a.u_bonus[b];
     int bonus;
     if constexpr (RJ > 0)
-        bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, rows, sh_f, sh_i);
+        bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, gsum);
     else if constexpr (RJ < 0)
         bonus = bonus_streamed_vec(a, rr, M, invS, c, ub, wtot, redi);
     else
