@@ -467,9 +467,15 @@ def commit_accepted_paged(k, v, hidden, best_beam, accept_len, k_pages, v_pages,
     Logical position t of request b is row t % page_size of page
     block_table[b, t // page_size]; the capacity is max_pages * page_size.
     Same rows, same hidden state, same overflow rule as commit_accepted.
+    A table entry that names no page of the pool (negative, or past the
+    pool) gives its positions nowhere to go, so a request that would write
+    one of them is treated like an overflow and left unchanged (the pages
+    describe no paged layout at all; this is the reading that never writes
+    a page the request does not own).
     """
     B, W, L = np.asarray(k).shape[:3]
     ps = k_pages.shape[2]
+    num_pages = k_pages.shape[0]
     cap = block_table.shape[1] * ps
     kp = np.array(k_pages, np.float64)
     vp = np.array(v_pages, np.float64)
@@ -479,6 +485,8 @@ def commit_accepted_paged(k, v, hidden, best_beam, accept_len, k_pages, v_pages,
     for b in range(B):
         w, n, c = int(best_beam[b]), int(accept_len[b]), int(kv_len[b])
         if not (0 <= w < W and 0 <= n <= L - 1 and 0 <= c and c + n + 1 <= cap):
+            continue
+        if not all(0 <= int(block_table[b, (c + j) // ps]) < num_pages for j in range(n + 1)):
             continue
         for j in range(n + 1):
             t = c + j

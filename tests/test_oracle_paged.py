@@ -120,3 +120,36 @@ def test_paged_commit_equals_contiguous_commit_through_the_gather():
     full = np.full(cfg.B, cfg.S, np.int32)
     np.testing.assert_array_equal(oracle.gather_pages(got["k_pages"], table, full), ref["k_cache"])
     np.testing.assert_array_equal(oracle.gather_pages(got["v_pages"], table, full), ref["v_cache"])
+
+
+@pytest.mark.parametrize("bad", [-1, 10_000])
+def test_paged_commit_with_a_table_entry_outside_the_pool_changes_nothing(bad):
+    """A request whose committed positions hit a table entry naming no page is left as it was;
+    the other requests commit as usual and no page of the pool changes for it."""
+    cfg = get_config("tiny_f32").with_(B=3, W=4, L=5, S=40, Hq=4, Hkv=2, D=8)
+    beams = draw_beams(cfg, 12)
+    nodes = unpacked_node_tensors(cfg, 12, beams)
+    kc = np.zeros((cfg.B, cfg.Hkv, cfg.S, cfg.D), np.float32)
+    vc = np.zeros_like(kc)
+    for b in range(cfg.B):
+        kc[b], vc[b] = kv_cache(cfg, 12, b)
+    ps = 8
+    kp, table = pool_from_cache(kc, ps)
+    vp, _ = pool_from_cache(vc, ps)
+    kv_len = np.array([13, 6, 20], np.int32)
+    best = np.array([1, 3, 2], np.int32)
+    n_acc = np.array([4, 2, 4], np.int32)
+    t2 = table.copy()
+    t2[0, (13 + 4) // ps] = bad          # request 0's last committed position has no page
+    t2[1, 4] = bad                       # an entry request 1 never reaches (positions 6..8)
+    got = oracle.commit_accepted_paged(nodes["k"], nodes["v"], nodes["hidden"], best, n_acc, kp, vp, t2, kv_len)
+    ref = oracle.commit_accepted_paged(nodes["k"], nodes["v"], nodes["hidden"], best, n_acc, kp, vp, table, kv_len)
+    np.testing.assert_array_equal(got["committed"], [False, True, True])
+    np.testing.assert_array_equal(got["kv_len"], [13, 9, 25])
+    assert np.isnan(got["hidden_next"][0]).all()
+    own0 = table[0]
+    np.testing.assert_array_equal(got["k_pages"][own0], kp[own0])
+    np.testing.assert_array_equal(got["v_pages"][own0], vp[own0])
+    others = np.setdiff1d(np.arange(kp.shape[0]), own0)
+    np.testing.assert_array_equal(got["k_pages"][others], ref["k_pages"][others])
+    np.testing.assert_array_equal(got["v_pages"][others], ref["v_pages"][others])
