@@ -3,13 +3,15 @@
 A step is the whole path: pack -> tree mask -> tree attention -> projection
 + argmax -> unpack + greedy accept, enqueued through the C ABI on one
 stream.  Inputs are resident in HBM before timing starts.  The workload
-defaults to the bf16 Llama-style setting (B=8, W=8, L=5, 32x128 heads,
-1024 cached tokens, vocabulary 32000); other settings are selectable.
+defaults to the largest single-GPU setting, the dedup sweep at p = 0.1
+(B=64 requests, W=64 beams of L=8 tokens, 32x128 heads, 2048 cached tokens,
+vocabulary 32000, bf16); the other settings are selectable.
 
 Prints one JSON line with the step throughput (candidate tokens/s), the
-roofline position of the dominant call and of tree attention (HIP events
-on the launch stream, inside the timed region), and the CPU oracle timed
-on a bounded sample on this host.
+roofline position of the dominant call, of tree attention and of the
+unpack gather (HIP events on the launch stream between the calls of the
+timed steps), and the CPU oracle timed on a bounded sample of requests on
+this host.
 """
 from __future__ import annotations
 
@@ -35,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama_mha")
+    ap.add_argument("--config", default="dedup_p0.1")
     ap.add_argument("--variant", choices=["full", "argmax-only"], default="full")
     ap.add_argument("--rotate-mb", type=float, default=1024.0,
                     help="rotate input sets until they exceed this many MB (defeats cache residency)")
@@ -43,18 +45,25 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="requests in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run a plain device copy of this size (a known-traffic reference for HBM counters)")
+    ap.add_argument("--legs", choices=["all", "step"], default="all",
+                    help="'step' times the verification step only (no commit/paged/ragged/stochastic legs)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure this box's streaming-copy rate and a vendor GEMM (torch.matmul) "
+                         "of the projection's shape, for comparison")
     return ap.parse_args()
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tree_attention_verification_rd_amd", "csrc")
-CALL_SOURCES = {"lm_head": "rd_lm_head.hip", "attention": "rd_attention.hip"}
+CALL_SOURCES = {"lm_head": "rd_lm_head.hip", "attention": "rd_attention.hip", "unpack": "rd_unpack_accept.hip"}
 
 
 def counted_traffic(workload: str, call: str):
     """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record for this workload (scaled by a copy of known size), or None when
-    there is no record or the kernel's sources changed since it was taken."""
+    there is no record or the kernel's sources changed since it was taken.
+    The counters cannot be read inside an ordinary run, so this value is the
+    record's, not a measurement of this run."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -66,20 +75,30 @@ def counted_traffic(workload: str, call: str):
     h = hashlib.sha256()
     for f in (CALL_SOURCES[call], "rd_common.h", "rd_internal.h"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
-    if rec.get(f"{call}.sources_sha256") != h.hexdigest()[:16]:
+    if rec.get(f"{call}.sources_sha256") != h.hexdigest()[:16] or f"{call}.traffic_bytes" not in rec:
         return None
     return int(rec[f"{call}.traffic_bytes"])
 
 
-def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool):
-    """Algorithmic traffic and work of each call (valid packed rows only; caches read once)."""
+def traffic_source(workload: str) -> str:
+    return f"profiles/{workload}_hbm_traffic.txt (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+
+
+def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool, depth=None):
+    """Algorithmic traffic and work of each call (valid packed rows only; caches read once).
+
+    Attention flops count 4*D per (query head, visible key): every cached key
+    plus the token's ancestors and itself (depth + 1 packed keys)."""
     R = int(plen.sum())
     e = 2 if cfg.dtype == "bf16" else 4
     D, Hq, Hkv, K, V = cfg.D, cfg.Hq, cfg.Hkv, cfg.hidden, cfg.V
     cache = int(kv_len.sum()) * Hkv * D * 2 * e
     attn_bytes = cache + R * Hkv * D * 2 * e + R * Hq * D * 2 * e
-    # visible keys per query: cache + ancestors (depth+1 ~ counted as the full tree path)
-    attn_flops = 4 * D * Hq * (int((plen * kv_len).sum()))
+    tree_keys = 0
+    if depth is not None:
+        for b in range(len(plen)):
+            tree_keys += int((depth[b, :plen[b]] + 1).sum())
+    attn_flops = 4 * D * Hq * (int((plen.astype(np.int64) * kv_len).sum()) + tree_keys)
     lm_bytes = V * K * e + R * K * e + (R * V * e if want_logits else 0)
     lm_flops = 2 * R * V * K
     cand = cfg.B * cfg.W * cfg.L
@@ -87,30 +106,108 @@ def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits:
     return {"attention": (attn_bytes, attn_flops), "lm_head": (lm_bytes, lm_flops), "unpack": (unpack_bytes, 0)}
 
 
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def baseline_requests(cfg, seed: int, sample: int):
+    """Requests the oracle runs: all of them for the small workloads, else
+    {0, B-1} plus seeded random ones up to `sample`."""
+    if cfg.candidates <= 400 or sample >= cfg.B:
+        return list(range(cfg.B))
+    req = [0, cfg.B - 1]
+    rng = np.random.default_rng(seed + 5)
+    while len(req) < max(sample, 2):
+        r = int(rng.integers(1, cfg.B - 1))
+        if r not in req:
+            req.append(r)
+    return sorted(req)
+
+
 def cpu_baseline(cfg, seed: int, sample: int):
-    """The oracle as it stands, on `sample` requests of the same workload."""
+    """The oracle as it stands (fp64 numpy, the unpacked per-candidate
+    definition) on a subset of the workload's requests, with numpy's BLAS
+    threads set to the host cores this process may use."""
     import oracle
     from synthetic import draw_beams, unpacked_node_tensors, kv_cache, lm_weight
+    cores = len(os.sched_getaffinity(0))
+    req = baseline_requests(cfg, seed, sample)
+    all_beams = draw_beams(cfg, seed)
+    beams = all_beams[req]
+    nodes = unpacked_node_tensors(cfg, seed, all_beams, requests=req)
+    kc = np.stack([kv_cache(cfg, seed, b)[0] for b in req])
+    vc = np.stack([kv_cache(cfg, seed, b)[1] for b in req])
+    w = lm_weight(cfg, seed)
+    kv = np.full(len(req), cfg.S, np.int32)
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    sub = cfg.with_(B=sample)
-    beams = draw_beams(sub, seed)
-    nodes = unpacked_node_tensors(sub, seed, beams)
-    kc = np.stack([kv_cache(sub, seed, b)[0] for b in range(sample)])
-    vc = np.stack([kv_cache(sub, seed, b)[1] for b in range(sample)])
-    w = lm_weight(sub, seed)
-    kv = np.full(sample, cfg.S, np.int32)
-    t0 = time.perf_counter()
-    res = oracle.verify_requests(beams, nodes["q"], nodes["k"], nodes["v"], kc, vc, kv, nodes["hidden"], w)
-    oracle.unpack(np.zeros((sample, cfg.P_max, 1)), res["pack"]["unpacker"])
-    dt = time.perf_counter() - t0
-    cand = sample * cfg.W * cfg.L
-    return {"value": cand / dt, "unit": "candidate tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{sample} of {cfg.B} requests of {cfg.name} (full step per request, fp64 numpy), "
-                      f"{dt:.1f} s"}
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    # the oracle's definition is per candidate: its logits are already in
+    # the unpacked [W, L, V] layout, so the step has no separate gather
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            oracle.verify_requests(beams, nodes["q"], nodes["k"], nodes["v"], kc, vc, kv, nodes["hidden"], w)
+            dt = time.perf_counter() - t0
+    else:  # pragma: no cover
+        t0 = time.perf_counter()
+        oracle.verify_requests(beams, nodes["q"], nodes["k"], nodes["v"], kc, vc, kv, nodes["hidden"], w)
+        dt = time.perf_counter() - t0
+    per_req = dt / len(req)
+    full = len(req) == cfg.B
+    value = cfg.W * cfg.L / per_req
+    how = "full batch" if full else (f"requests {req} of {cfg.B}; per-request time x B "
+                                      f"(extrapolated: requests are independent)")
+    return {"value": round(value, 2), "unit": "candidate tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{cfg.name}, {how}: full step per request (pack, mask, per-beam attention, fp64 "
+                      f"projection of every candidate, argmax, accept), {dt:.1f} s for {len(req)} requests"}
+
+
+def measure_peaks(cfg, s, torch, dev, plen_rows: int):
+    """This box's reference rates: a plain device copy (torch copy_ of 2 GB,
+    source pushed out of the last-level cache by a 1 GB fill between
+    copies) and the vendor GEMM (torch.matmul, hipBLASLt) of the
+    projection's shape, [R, K] x [K, V] for R valid packed rows."""
+    def timed(fn, reps, prep=None):
+        ts = []
+        for _ in range(reps):
+            if prep is not None:
+                prep()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    n = 2_000_000_000 // 4
+    src_t = torch.ones(n, dtype=torch.float32, device=dev)
+    dst_t = torch.empty_like(src_t)
+    flush = torch.empty(250_000_000, dtype=torch.float32, device=dev)
+    t_copy = timed(lambda: dst_t.copy_(src_t), 5, lambda: flush.fill_(1.0))
+    del src_t, dst_t, flush
+    K, V = cfg.hidden, cfg.V
+    x = s["hidden"].reshape(-1, K)[:plen_rows].contiguous()
+    wt = s["weight"].t().contiguous()  # [K, V]: a plain (non-batched) product
+    for _ in range(2):
+        torch.matmul(x, wt)
+    torch.cuda.synchronize()
+    t_mm = timed(lambda: torch.matmul(x, wt), 10)
+    del x, wt
+    torch.cuda.synchronize()
+    return {"copy_GBs": round(2 * n * 4 / t_copy / 1e9, 1),
+            "vendor_gemm": {"call": "torch.matmul (hipBLASLt), projection shape", "M": plen_rows, "N": V, "K": K,
+                            "us": round(t_mm * 1e6, 1),
+                            "TFLOPs": round(2 * plen_rows * V * K / t_mm / 1e12, 1)}}
 
 
 def make_sets(cfg, n_sets, seed, dev, dt):
@@ -193,32 +290,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst, flush
 
+    peaks = None
+    if args.peaks:
+        step(sets[0])
+        torch.cuda.synchronize()
+        peaks = measure_peaks(cfg, sets[0], torch, dev, int(pk["length"].sum().item()))
+
     for i in range(args.warmup):
         step(sets[i % n_sets])
     torch.cuda.synchronize()
 
     K = args.steps
-    # Timed region: K whole steps, bracketed by synchronisation, with no
-    # per-call markers inside (each event record costs the GPU ~3 us).
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps, bracketed by synchronisation.  A HIP event
+    # on the launch stream (torch's current stream, which the binding passes
+    # to every call) sits between consecutive calls, so the per-call
+    # durations come from the timed steps themselves; at this size each event
+    # costs the GPU a few microseconds of a step of milliseconds.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_start.record()
-    for i in range(K):
-        step(sets[i % n_sets])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_gpu = t_start.elapsed_time(t_end) / K
-    ms_per_step = max(wall * 1e3 / K, ms_gpu)
-
-    # Per-call durations: the same K steps again, with a HIP event on the
-    # launch stream between consecutive calls.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     for i in range(K):
         step(sets[i % n_sets], evs[i])
     torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_gpu = evs[0][0].elapsed_time(evs[K - 1][5]) / K
+    ms_per_step = max(wall * 1e3 / K, ms_gpu)
     marks = {"pack_mask": (0, 2), "attention": (2, 3), "lm_head": (3, 4), "unpack_accept": (4, 5)}
     per_call_us = {n: float(np.mean([e[j0].elapsed_time(e[j1]) for e in evs]) * 1e3) for n, (j0, j1) in marks.items()}
 
@@ -254,108 +350,121 @@ def main():
         torch.cuda.synchronize()
         return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
 
-    # The commit of the accepted path, the call after the step (not part of
-    # the timed step): at full acceptance (n = L-1 on beam 0) every request
-    # appends L rows per KV head; call i advances its own kv_len row.
-    c_best = torch.zeros(B, dtype=torch.int32, device=dev)
-    c_nacc = torch.full((B,), cfg.L - 1, dtype=torch.int32, device=dev)
-    c_kv = torch.empty((K, B), dtype=torch.int32, device=dev)
-    c_hid = torch.empty((B, cfg.hidden), dtype=dt, device=dev)
+    extras = {}
+    if args.legs == "all":
+        # The commit of the accepted path, the call after the step (not part of
+        # the timed step): at full acceptance (n = L-1 on beam 0) every request
+        # appends L rows per KV head; call i advances its own kv_len row.
+        c_best = torch.zeros(B, dtype=torch.int32, device=dev)
+        c_nacc = torch.full((B,), cfg.L - 1, dtype=torch.int32, device=dev)
+        c_kv = torch.empty((K, B), dtype=torch.int32, device=dev)
+        c_hid = torch.empty((B, cfg.hidden), dtype=dt, device=dev)
 
-    def commit_call(i):
-        s = sets[i % n_sets]
-        rd.rd_commit_accepted(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], s["k_cache"], s["v_cache"],
-                              c_kv[i], s["hidden"], hidden_next=c_hid)
+        def commit_call(i):
+            s = sets[i % n_sets]
+            rd.rd_commit_accepted(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], s["k_cache"], s["v_cache"],
+                                  c_kv[i], s["hidden"], hidden_next=c_hid)
 
-    commit_us = queued_call_us(commit_call, lambda: c_kv.fill_(cfg.S - cfg.L))
+        commit_us = queued_call_us(commit_call, lambda: c_kv.fill_(cfg.S - cfg.L))
 
-    # Tree attention over a paged cache (the same keys, cut into 64-token
-    # pages of a pool in random order, one pool per input set).
-    ps = 64
-    npg = (cfg.S + ps - 1) // ps
-    pools = []
-    for si, s in enumerate(sets):
-        gperm = torch.Generator()
-        gperm.manual_seed(1000 + si)
-        perm = torch.randperm(B * npg, generator=gperm).to(dev)
-        pool = []
-        for c in (s["k_cache"], s["v_cache"]):
-            cp = torch.nn.functional.pad(c, (0, 0, 0, npg * ps - cfg.S)) if npg * ps != cfg.S else c
-            cut = cp.reshape(B, cfg.Hkv, npg, ps, cfg.D).permute(0, 2, 1, 3, 4).reshape(B * npg, cfg.Hkv, ps, cfg.D)
-            p_ = torch.empty_like(cut)
-            p_[perm] = cut
-            pool.append(p_)
-        pools.append((pool[0], pool[1], perm.reshape(B, npg).to(torch.int32).contiguous()))
-    paged_ws = torch.empty(max(rd.rd_tree_attention_workspace_size(1 if cfg.dtype == "bf16" else 0, B, P, cfg.Hq,
-                                                                  cfg.Hkv, cfg.D, npg * ps), 1),
-                           dtype=torch.uint8, device=dev)
-    paged_out = torch.empty_like(bufs.attn)
+        # Tree attention over a paged cache (the same keys, cut into 64-token
+        # pages of a pool in random order, one pool per input set).
+        ps = 64
+        npg = (cfg.S + ps - 1) // ps
+        pools = []
+        for si, s in enumerate(sets):
+            gperm = torch.Generator()
+            gperm.manual_seed(1000 + si)
+            perm = torch.randperm(B * npg, generator=gperm).to(dev)
+            pool = []
+            for c in (s["k_cache"], s["v_cache"]):
+                cp = torch.nn.functional.pad(c, (0, 0, 0, npg * ps - cfg.S)) if npg * ps != cfg.S else c
+                cut = cp.reshape(B, cfg.Hkv, npg, ps, cfg.D).permute(0, 2, 1, 3, 4).reshape(B * npg, cfg.Hkv, ps, cfg.D)
+                p_ = torch.empty_like(cut)
+                p_[perm] = cut
+                pool.append(p_)
+            pools.append((pool[0], pool[1], perm.reshape(B, npg).to(torch.int32).contiguous()))
+        paged_ws = torch.empty(max(rd.rd_tree_attention_workspace_size(1 if cfg.dtype == "bf16" else 0, B, P, cfg.Hq,
+                                                                      cfg.Hkv, cfg.D, npg * ps), 1),
+                               dtype=torch.uint8, device=dev)
+        paged_out = torch.empty_like(bufs.attn)
 
-    def paged_call(i):
-        s = sets[i % n_sets]
-        kp, vp, tbl = pools[i % n_sets]
-        rd.rd_tree_attention_paged(s["q"], s["k_new"], s["v_new"], kp, vp, tbl, kv_len, bufs.mask, pk["length"],
-                                   out=paged_out, workspace=paged_ws)
+        def paged_call(i):
+            s = sets[i % n_sets]
+            kp, vp, tbl = pools[i % n_sets]
+            rd.rd_tree_attention_paged(s["q"], s["k_new"], s["v_new"], kp, vp, tbl, kv_len, bufs.mask, pk["length"],
+                                       out=paged_out, workspace=paged_ws)
 
-    paged_us = queued_call_us(paged_call, lambda: None)
+        paged_us = queued_call_us(paged_call, lambda: None)
 
-    def commit_paged_call(i):
-        s = sets[i % n_sets]
-        kp, vp, tbl = pools[i % n_sets]
-        rd.rd_commit_accepted_paged(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], kp, vp, tbl, c_kv[i],
-                                    s["hidden"], hidden_next=c_hid)
+        def commit_paged_call(i):
+            s = sets[i % n_sets]
+            kp, vp, tbl = pools[i % n_sets]
+            rd.rd_commit_accepted_paged(pk["unpacker"], c_best, c_nacc, s["k_new"], s["v_new"], kp, vp, tbl, c_kv[i],
+                                        s["hidden"], hidden_next=c_hid)
 
-    commit_paged_us = queued_call_us(commit_paged_call, lambda: c_kv.fill_(cfg.S - cfg.L))
+        commit_paged_us = queued_call_us(commit_paged_call, lambda: c_kv.fill_(cfg.S - cfg.L))
 
-    # Ragged batch: the same beams with seeded per-request beam counts and
-    # lengths (1..W, 1..L), through the two calls whose work depends on them.
-    rng_r = np.random.default_rng(seed + 17)
-    r_bw = torch.from_numpy(rng_r.integers(1, cfg.W + 1, size=B).astype(np.int32)).to(dev)
-    r_bl = torch.from_numpy(rng_r.integers(1, cfg.L + 1, size=B).astype(np.int32)).to(dev)
-    r_pk = {k: torch.empty_like(v) for k, v in pk.items()}
-    r_mask = torch.empty_like(bufs.mask)
-    r_acc = {k: torch.empty_like(v) for k, v in bufs.accept.items()}
+        # Ragged batch: the same beams with seeded per-request beam counts and
+        # lengths (1..W, 1..L), through the two calls whose work depends on them.
+        rng_r = np.random.default_rng(seed + 17)
+        r_bw = torch.from_numpy(rng_r.integers(1, cfg.W + 1, size=B).astype(np.int32)).to(dev)
+        r_bl = torch.from_numpy(rng_r.integers(1, cfg.L + 1, size=B).astype(np.int32)).to(dev)
+        r_pk = {k: torch.empty_like(v) for k, v in pk.items()}
+        r_mask = torch.empty_like(bufs.mask)
+        r_acc = {k: torch.empty_like(v) for k, v in bufs.accept.items()}
 
-    def ragged_pack_call(i):
-        rd.rd_pack_beams_mask(beams, packed_tokens=r_pk["tokens"], packed_len=r_pk["length"],
-                              unpacker=r_pk["unpacker"], packed_depth=r_pk["depth"], packed_src=r_pk["src"],
-                              mask=r_mask, beam_width=r_bw, beam_len=r_bl)
+        def ragged_pack_call(i):
+            rd.rd_pack_beams_mask(beams, packed_tokens=r_pk["tokens"], packed_len=r_pk["length"],
+                                  unpacker=r_pk["unpacker"], packed_depth=r_pk["depth"], packed_src=r_pk["src"],
+                                  mask=r_mask, beam_width=r_bw, beam_len=r_bl)
 
-    def ragged_accept_call(i):
-        rd.rd_unpack_accept(beams, r_pk["unpacker"], bufs.argmax, bufs.logits if full else None,
-                            unpacked=bufs.unpacked, beam_width=r_bw, beam_len=r_bl, **r_acc)
+        def ragged_accept_call(i):
+            rd.rd_unpack_accept(beams, r_pk["unpacker"], bufs.argmax, bufs.logits if full else None,
+                                unpacked=bufs.unpacked, beam_width=r_bw, beam_len=r_bl, **r_acc)
 
-    # Stochastic step 4 on the step's own logits (full variant), with a
-    # seeded draft distribution and uniforms.
-    stoch_us = None
-    if full:
-        gq = torch.Generator(device=dev)
-        gq.manual_seed(seed + 23)
-        s_q = torch.softmax(torch.randn((B, P, cfg.V), generator=gq, device=dev), dim=-1)
-        s_ua = torch.rand((B, cfg.L, cfg.W), generator=gq, device=dev)
-        s_ub = torch.rand((B,), generator=gq, device=dev)
-        s_ws = torch.empty(max(rd.rd_stochastic_accept_workspace_size(B, cfg.W, cfg.L), 1), dtype=torch.uint8,
-                           device=dev)
-        s_out = {k: torch.empty_like(v) for k, v in bufs.accept.items() if k != "match_len"}
-        s_path = torch.empty_like(bufs.accept["accepted_tokens"])
+        # Stochastic step 4 on the step's own logits (full variant), with a
+        # seeded draft distribution and uniforms.
+        stoch_us = None
+        if full:
+            gq = torch.Generator(device=dev)
+            gq.manual_seed(seed + 23)
+            s_q = torch.softmax(torch.randn((B, P, cfg.V), generator=gq, device=dev), dim=-1)
+            s_ua = torch.rand((B, cfg.L, cfg.W), generator=gq, device=dev)
+            s_ub = torch.rand((B,), generator=gq, device=dev)
+            s_ws = torch.empty(max(rd.rd_stochastic_accept_workspace_size(B, cfg.W, cfg.L), 1), dtype=torch.uint8,
+                               device=dev)
+            s_out = {k: torch.empty_like(v) for k, v in bufs.accept.items() if k != "match_len"}
+            s_path = torch.empty_like(bufs.accept["accepted_tokens"])
 
-        def stoch_call(i):
-            rd.rd_stochastic_accept(pk["unpacker"], pk["length"], pk["tokens"], bufs.logits, s_q, s_ua, s_ub,
-                                    path=s_path, workspace=s_ws, **s_out)
+            def stoch_call(i):
+                rd.rd_stochastic_accept(pk["unpacker"], pk["length"], pk["tokens"], bufs.logits, s_q, s_ua, s_ub,
+                                        path=s_path, workspace=s_ws, **s_out)
 
-        stoch_us = queued_call_us(stoch_call, lambda: None)
+            stoch_us = queued_call_us(stoch_call, lambda: None)
 
-    ragged_pack_us = queued_call_us(ragged_pack_call, lambda: None)
-    ragged_accept_us = queued_call_us(ragged_accept_call, lambda: None)
-    ragged_packed = int(r_pk["length"].sum().item())
-    contig_us = queued_call_us(lambda i: rd.rd_tree_attention(
-        sets[i % n_sets]["q"], sets[i % n_sets]["k_new"], sets[i % n_sets]["v_new"], sets[i % n_sets]["k_cache"],
-        sets[i % n_sets]["v_cache"], kv_len, bufs.mask, pk["length"], out=paged_out, workspace=bufs.attn_ws),
-        lambda: None)
-    commit_bytes = 2 * (2 * B * cfg.Hkv * cfg.L * cfg.D + B * cfg.hidden) * esz   # read + write
+        ragged_pack_us = queued_call_us(ragged_pack_call, lambda: None)
+        ragged_accept_us = queued_call_us(ragged_accept_call, lambda: None)
+        ragged_packed = int(r_pk["length"].sum().item())
+        contig_us = queued_call_us(lambda i: rd.rd_tree_attention(
+            sets[i % n_sets]["q"], sets[i % n_sets]["k_new"], sets[i % n_sets]["v_new"], sets[i % n_sets]["k_cache"],
+            sets[i % n_sets]["v_cache"], kv_len, bufs.mask, pk["length"], out=paged_out, workspace=bufs.attn_ws),
+            lambda: None)
+        commit_bytes = 2 * (2 * B * cfg.Hkv * cfg.L * cfg.D + B * cfg.hidden) * esz   # read + write
+        extras = {
+            "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
+                           "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
+            "stochastic": {"call": "rd_stochastic_accept",
+                           "avg_us": None if stoch_us is None else round(stoch_us, 2)},
+            "ragged": {"calls": "rd_pack_beams_mask_ragged + rd_unpack_accept_ragged",
+                       "candidates": int((r_bw * r_bl).sum().item()), "packed_tokens": ragged_packed,
+                       "pack_mask_us": round(ragged_pack_us, 2), "unpack_accept_us": round(ragged_accept_us, 2)},
+            "attention_paged": {"call": "rd_tree_attention_paged", "page_size": ps, "avg_us": round(paged_us, 2),
+                                "contiguous_avg_us": round(contig_us, 2)},
+        }
 
     plen = pk["length"].cpu().numpy()
-    work = step_bytes_and_flops(cfg, plen, kv_len_np, full)
+    work = step_bytes_and_flops(cfg, plen, kv_len_np, full, pk["depth"].cpu().numpy())
     cand = B * cfg.W * cfg.L
 
     def roof(call, bound):
@@ -378,6 +487,12 @@ def main():
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         return "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12) else "mfma"
 
+    def binding_frac(call):
+        """max(bytes at peak HBM, flops at peak MFMA) / measured: the fraction of the call's own roof."""
+        nbytes, flops = work[call]
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        return max(nbytes / (PEAK_HBM_GBS * 1e9), flops / (peak * 1e12)) / (per_call_us[call] * 1e-6)
+
     dominant = max(("attention", "lm_head"), key=lambda c: per_call_us[c])
     line = {
         "metric": "verified candidate tokens/sec per verify step; attention HBM GB/s % peak",
@@ -392,24 +507,31 @@ def main():
                    "packed_tokens": int(plen.sum()), "candidates": cand, "input_sets_rotated": n_sets},
         "roofline": {"kernel": f"rd_{'lm_head_argmax' if dominant == 'lm_head' else 'tree_attention'}",
                      **roof(dominant, bound_of(dominant))},
-        "attention_hbm": {"kernel": "rd_tree_attention", **roof("attention", "hbm")},
+        "attention_hbm": {"kernel": "rd_tree_attention", **roof("attention", "hbm"),
+                          "algorithmic_flops": int(work["attention"][1]),
+                          "binding_roof_frac": round(binding_frac("attention"), 4)},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "gpu_ms_per_step": round(ms_gpu, 4),
-        "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
-                       "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
-        "stochastic": {"call": "rd_stochastic_accept", "avg_us": None if stoch_us is None else round(stoch_us, 2)},
-        "ragged": {"calls": "rd_pack_beams_mask_ragged + rd_unpack_accept_ragged",
-                   "candidates": int((r_bw * r_bl).sum().item()), "packed_tokens": ragged_packed,
-                   "pack_mask_us": round(ragged_pack_us, 2), "unpack_accept_us": round(ragged_accept_us, 2)},
-        "attention_paged": {"call": "rd_tree_attention_paged", "page_size": ps, "avg_us": round(paged_us, 2),
-                            "contiguous_avg_us": round(contig_us, 2),
-                            "achieved": round(work["attention"][0] / (paged_us * 1e-6) / 1e9, 1),
-                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(work["attention"][0] / (paged_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    if full:
+        nb = work["unpack"][0]
+        ach = nb / (per_call_us["unpack_accept"] * 1e-6) / 1e9
+        line["gather_hbm"] = {"kernel": "rd_unpack_accept", "bound": "hbm", "achieved": round(ach, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                              "traffic": counted_traffic(cfg.name, "unpack"), "algorithmic_bytes": int(nb),
+                              "avg_us": round(per_call_us["unpack_accept"], 2)}
+    if "attention_paged" in extras:
+        ap_ = extras["attention_paged"]
+        ach = work["attention"][0] / (ap_["avg_us"] * 1e-6) / 1e9
+        ap_.update({"achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4)})
+    line.update(extras)
+    if any(line[k].get("traffic") is not None for k in ("roofline", "attention_hbm", "gather_hbm") if k in line):
+        line["traffic_source"] = traffic_source(cfg.name)
+    if peaks is not None:
+        line["peaks_on_box"] = peaks
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or (B if cfg.candidates <= 400 else 2)
-        line["cpu_baseline"] = cpu_baseline(cfg, seed, min(sample, B))
+        line["cpu_baseline"] = cpu_baseline(cfg, seed, args.cpu_sample or 3)
     print(json.dumps(line), flush=True)
 
 

@@ -42,7 +42,8 @@
  *   - Device-side contents (kv_len <= S_max, unpacker values in [0,P_max))
  *     are trusted as produced by rd_pack_beams; kernels clamp every index
  *     they derive from them so a bad value cannot address outside the
- *     arrays, but the results are then unspecified.
+ *     arrays, but the results are then unspecified.  Debug mode
+ *     (rd_set_debug) checks them first and returns RD_E_CONTENT instead.
  *   - Results are deterministic: identical inputs give bit-identical outputs
  *     (no floating-point atomics, fixed reduction orders).
  *   - The library keeps no state between calls and is safe to call from
@@ -65,7 +66,8 @@ enum rd_status_code {
     RD_E_ARG = -1,
     RD_E_UNSUPPORTED = -2,
     RD_E_WORKSPACE = -3,
-    RD_E_HIP = -4
+    RD_E_HIP = -4,
+    RD_E_CONTENT = -5  /* debug mode only: a device-side value is out of range */
 };
 
 enum rd_dtype {
@@ -81,6 +83,44 @@ const char *rd_status_string(int status);
 
 /* Library version, major*10000 + minor*100 + patch. */
 int rd_version(void);
+
+/*
+ * Tuning knobs (for tests and measurements; not needed in production).
+ * Each forces a choice the library otherwise makes itself; 0 restores the
+ * automatic choice.  Knobs are process-wide, read by every later call
+ * (workspace-size queries included: query after setting), and not
+ * synchronised with calls already running on other host threads.
+ *   RD_KNOB_ATTN_SPLITS  n >= 1: split each (request, KV head)'s cache
+ *                        into n parts (clamped to the key tiles), merged
+ *                        by log-sum-exp; bf16 attention only.
+ *   RD_KNOB_ATTN_FEWROW  1: lane-interleaved eight-wavefront shape for at
+ *                        most 64 rows per (request, KV head); 2: the
+ *                        four-wavefront shape.  bf16 attention only.
+ *   RD_KNOB_LM_SHAPE     1: the few-row projection tile shape; 2: the
+ *                        many-row shape.  bf16 projection only.
+ * Returns the previous value, or RD_E_ARG for an unknown knob or a
+ * negative value.
+ */
+enum rd_knob {
+    RD_KNOB_ATTN_SPLITS = 1,
+    RD_KNOB_ATTN_FEWROW = 2,
+    RD_KNOB_LM_SHAPE = 3,
+    RD_KNOB_COUNT = 4
+};
+int rd_set_knob(int knob, int value);
+
+/*
+ * Debug mode (also switched on by RD_DEBUG=1 in the environment when the
+ * library is first used).  Every entry point then checks, before launching
+ * its kernels, the device-side values it otherwise trusts: kv_len in
+ * [0, S_max], packed_len in [0, P_max], unpacker slots in [-1, P_max), and
+ * the block-table entries of every cached position in [0, num_pages).  The
+ * checks run on `stream`, the host waits for them, and a bad value makes
+ * the call return RD_E_CONTENT with nothing else launched.  Debug mode
+ * therefore synchronises the host on every call.  Returns the previous
+ * setting (0 or 1).
+ */
+int rd_set_debug(int on);
 
 /*
  * Step 1 -- pack: remove shared prefixes across each request's beams.
@@ -344,7 +384,10 @@ int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_b
  * rd_tree_attention_paged): logical position t = kv_len[b] + j goes to row
  * t % page_size of page block_table[b, t / page_size]; the capacity is
  * max_pages * page_size.  The caller gives every request table entries for
- * the positions it may commit; page ids are clamped to [0, num_pages).
+ * the positions it may commit.  A request whose committed positions reach a
+ * table entry outside [0, num_pages) (e.g. -1 for "no page yet") is left
+ * unchanged, like an overflow: its kv_len does not move and no page is
+ * written, so a commit never writes into a page it was not given.
  * Same rows, hidden state, overflow rule, launch count and errors as
  * rd_commit_accepted, plus RD_E_ARG for page_size < 1, negative num_pages
  * or max_pages, or a null pool or table.

@@ -85,14 +85,17 @@ class Problem:
     """One verification-step problem on the device plus the oracle's view of the checked requests."""
 
     def __init__(self, cfg: Config, seed: int, checked=None, beams_mode="workload", plant=False,
-                 device="cuda", kv_len=None, beams=None):
+                 device="cuda", kv_len=None, beams=None, beam_width=None, beam_len=None):
         t0 = time.time()
         self.cfg, self.seed = cfg, seed
         B, W, L, P = cfg.B, cfg.W, cfg.L, cfg.P_max
         self.checked = list(range(B)) if checked is None else sorted(set(checked))
         self.beams = draw_beams(cfg, seed, beams_mode) if beams is None else np.asarray(beams, np.int32)
         self.kv_len = kv_lengths(cfg) if kv_len is None else np.asarray(kv_len, np.int32)
-        self.pack = oracle.pack_beams(self.beams)
+        # ragged batches: per-request beam count and length (None: every request is full)
+        self.beam_width = None if beam_width is None else np.asarray(beam_width, np.int32)
+        self.beam_len = None if beam_len is None else np.asarray(beam_len, np.int32)
+        self.pack = oracle.pack_beams(self.beams, self.beam_width, self.beam_len)
         dt = torch_dtype(cfg)
         dev = torch.device(device)
         self.weight_np = lm_weight(cfg, seed)
@@ -157,8 +160,12 @@ class Problem:
         """Force the target along a prefix of one beam: target(w*, j) = beams[w*, j+1] for j < n*."""
         cfg = self.cfg
         rng = np.random.default_rng(self.seed * 131 + b)
-        w_star = int(rng.integers(0, cfg.W))
-        n_star = int(rng.integers(1, cfg.L)) if cfg.L > 1 else 0
+        W, L = cfg.W, cfg.L
+        if self.beam_width is not None:     # plant inside the request's own beams
+            W = int(min(max(self.beam_width[b], 1), cfg.W))
+            L = int(min(max(self.beam_len[b], 1), cfg.L))
+        w_star = int(rng.integers(0, W))
+        n_star = int(rng.integers(1, L)) if L > 1 else 0
         # raises the target logit by about 12, far above the ~4 sigma maximum of the random logits
         scale = 12.0 / (cfg.hidden * 0.02 ** 2)
         plants = {}
@@ -177,7 +184,25 @@ class Problem:
         return oracle.lm_head_logits(self.h_unp, self.weight64)
 
     def oracle_accept(self, target_unp):
-        return oracle.greedy_accept(self.beams[self.checked], target_unp)
+        sub = self.checked
+        if self.beam_width is None:
+            return oracle.greedy_accept(self.beams[sub], target_unp)
+        return oracle.greedy_accept(self.beams[sub], target_unp, self.beam_width[sub], self.beam_len[sub])
+
+    def oracle_target(self):
+        """Greedy target token of every candidate of the checked requests (fp64 oracle logits)."""
+        return oracle.argmax_first(self.oracle_logits())
+
+    def oracle_mask_bits(self):
+        """The oracle's tree-mask words of every request."""
+        return oracle.mask_to_bits(oracle.tree_mask(self.pack["unpacker"], self.pack["length"]))
+
+    def assert_pack_matches(self, pk, mask=None):
+        """GPU pack (and mask) bit-exact against the oracle's on every request."""
+        for key in ("tokens", "length", "unpacker"):
+            np.testing.assert_array_equal(pk[key].cpu().numpy(), self.pack[key], err_msg=f"pack {key}")
+        if mask is not None:
+            np.testing.assert_array_equal(mask_words_np(mask), self.oracle_mask_bits(), err_msg="mask")
 
 
 def normwise_rows(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

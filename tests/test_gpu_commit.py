@@ -4,7 +4,10 @@ After a verification step, the best beam's accepted keys/values are appended
 to the cache and kv_len advances.  Every compared value is a copy, so every
 comparison is bit-exact: against the oracle on the requests it checks, and on
 every request against the expected cache built with torch indexing from the
-packed inputs (rows outside the accepted path must be untouched).
+packed inputs (rows outside the accepted path must be untouched).  The
+step's pack and, on the checked requests, its accept are first asserted
+equal to the oracle's (fp64 targets), and the oracle's commit is fed the
+oracle's own accept.
 """
 import sys
 
@@ -79,6 +82,13 @@ def test_commit_after_verify_step(name):
     res = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t,
                          prob.hidden, prob.weight, want_logits=False)
     un, best, nacc = res["pack"]["unpacker"], res["best_beam"], res["accept_len"]
+    # the step's pack on every request and its accept on the checked requests are the oracle's
+    # before anything below builds on them
+    prob.assert_pack_matches(res["pack"])
+    sub = prob.checked
+    acc = prob.oracle_accept(prob.oracle_target())
+    for key in ("best_beam", "accept_len", "accepted_tokens"):
+        np.testing.assert_array_equal(res[key].cpu().numpy()[sub], acc[key], err_msg=key)
     exp_k, exp_len = expected_commit(un, best, nacc, prob.k_new, prob.k_cache, prob.kv_len_t)
     exp_v, _ = expected_commit(un, best, nacc, prob.v_new, prob.v_cache, prob.kv_len_t)
     say(f"[commit] {name}: step done, accept_len {nacc.cpu().numpy()[:8].tolist()}; committing")
@@ -98,10 +108,10 @@ def test_commit_after_verify_step(name):
     unp = un.cpu().numpy()
     for b in np.nonzero(moved)[0]:
         assert torch.equal(hnext[b], prob.hidden[b, int(unp[b, bb[b], na[b]])])
-    # checked requests: against the oracle, which reads the unpacked per-candidate tensors
-    sub = prob.checked
-    ref = oracle.commit_accepted(prob.k_unp, prob.v_unp, prob.h_unp, bb[sub], na[sub], prob.kc_np, prob.vc_np,
-                                 prob.kv_len[sub])
+    # checked requests: against the oracle's commit of the oracle's own accept, which reads the
+    # unpacked per-candidate tensors
+    ref = oracle.commit_accepted(prob.k_unp, prob.v_unp, prob.h_unp, acc["best_beam"], acc["accept_len"],
+                                 prob.kc_np, prob.vc_np, prob.kv_len[sub])
     np.testing.assert_array_equal(kv_dev.cpu().numpy()[sub], ref["kv_len"])
     np.testing.assert_array_equal(moved[sub], ref["committed"])
     for i, b in enumerate(sub):

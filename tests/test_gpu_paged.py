@@ -5,7 +5,10 @@ permuted at random, with extra unreferenced pages and table entries past
 each cache length set to -1 (never read).  Where the contiguous kernel
 walks the same key order (one split), the paged result must equal
 rd_tree_attention's bit for bit; everywhere it must match the oracle's
-paged attention to the usual normwise tolerance.
+paged attention (with the oracle's own mask) and the per-beam definition to
+the usual normwise tolerance.  The paged commit is compared with the
+oracle's paged commit of the oracle's own accept, and a table entry naming
+no page must leave its request and the pool untouched.
 """
 import sys
 
@@ -72,16 +75,12 @@ def logical_from_pool(pool, table, S):
     return rows.reshape(B, pool.shape[1], n * ps, pool.shape[3])[:, :, :S]
 
 
-def oracle_paged(prob_q, k_new, v_new, k_pool, v_pool, table, kv_len, mask_t, plen_t):
-    """The oracle's paged attention on the device inputs (fp64 copies)."""
-    B = prob_q.shape[0]
-    mask_bits = mask_t.cpu().numpy().view(np.uint32)
-    P = prob_q.shape[1]
-    mask = np.zeros((B, P, P), bool)
-    for q in range(P):
-        mask[:, :, q] = (mask_bits[:, :, q // 32] >> (q % 32)) & 1
-    return oracle.attention_paged(to_np(prob_q), to_np(k_new), to_np(v_new), to_np(k_pool), to_np(v_pool),
-                                  table.cpu().numpy(), kv_len.cpu().numpy(), mask, plen_t.cpu().numpy())
+def oracle_paged(prob, k_pool, v_pool, table):
+    """The oracle's paged attention with the oracle's own mask and packed lengths, on the
+    packed inputs of `prob` and the pools (fp64 copies)."""
+    mask = oracle.tree_mask(prob.pack["unpacker"], prob.pack["length"])
+    return oracle.attention_paged(to_np(prob.q), to_np(prob.k_new), to_np(prob.v_new), to_np(k_pool),
+                                  to_np(v_pool), table.cpu().numpy(), prob.kv_len, mask, prob.pack["length"])
 
 
 SMALL = {
@@ -102,8 +101,11 @@ def test_paged_small(name):
     prob = Problem(base, base_seed(base, 4), kv_len=np.array(kvl, np.int32))
     pk = rd.rd_pack_beams(prob.beams_t)
     mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+    torch.cuda.synchronize()
+    prob.assert_pack_matches(pk, mask)   # the mask the kernels read is the oracle's
     ref = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t, mask,
                                pk["length"])
+    per_beam = prob.oracle_attention()   # the plain definition: each candidate over its own beam
     for ps in page_sizes:
         k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, ps, seed=ps)
         got = rd.rd_tree_attention_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, prob.kv_len_t,
@@ -112,13 +114,14 @@ def test_paged_small(name):
         plan_split = name == "split"
         if not plan_split:
             assert torch.equal(got, ref), f"{name} ps={ps}: paged differs from contiguous"
-        want = oracle_paged(prob.q, prob.k_new, prob.v_new, k_pool, v_pool, table, prob.kv_len_t, mask,
-                            pk["length"])
-        plen = pk["length"].cpu().numpy()
+        want = oracle_paged(prob, k_pool, v_pool, table)
+        plen = prob.pack["length"]
         errs = np.concatenate([normwise_rows(to_np(got[b, :plen[b]]), want[b, :plen[b]]).ravel()
                                for b in range(base.B)])
-        say(f"[paged] {name} ps={ps}: oracle normwise error {fmt_err(errs)}")
-        assert errs.max() <= TOL[base.dtype]
+        un = prob.pack["unpacker"]
+        errs_pb = np.concatenate([normwise_rows(to_np(got[b])[un[b]], per_beam[b]).ravel() for b in range(base.B)])
+        say(f"[paged] {name} ps={ps}: oracle paged normwise {fmt_err(errs)}, per-beam {fmt_err(errs_pb)}")
+        assert errs.max() <= TOL[base.dtype] and errs_pb.max() <= TOL[base.dtype]
         for b in range(base.B):
             assert (got[b, plen[b]:] == 0).all()
 
@@ -130,6 +133,8 @@ def test_paged_full_size(name, split_exact):
     prob = Problem(cfg, base_seed(cfg), checked=[0])
     pk = rd.rd_pack_beams(prob.beams_t)
     mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+    torch.cuda.synchronize()
+    prob.assert_pack_matches(pk, mask)
     ref = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t, mask,
                                pk["length"])
     k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, 64, seed=1)
@@ -178,8 +183,15 @@ def test_paged_commit_then_attention(name, ps):
     res = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t,
                          prob.hidden, prob.weight, want_logits=False)
     un, best, nacc = res["pack"]["unpacker"], res["best_beam"], res["accept_len"]
+    prob.assert_pack_matches(res["pack"], res["mask"])
+    acc = prob.oracle_accept(prob.oracle_target())
+    for key in ("best_beam", "accept_len"):
+        np.testing.assert_array_equal(res[key].cpu().numpy(), acc[key], err_msg=key)
     k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, ps, seed=5,
                                       unread_to_minus_one=False)
+    # the oracle's paged commit of its own accept, on the pools as they are before the commit
+    want = oracle.commit_accepted_paged(prob.k_unp, prob.v_unp, prob.h_unp, acc["best_beam"], acc["accept_len"],
+                                        to_np(k_pool), to_np(v_pool), table.cpu().numpy(), prob.kv_len)
     untouched = [i for i in range(k_pool.shape[0]) if i not in set(table.cpu().numpy().ravel().tolist())]
     spare_k, spare_v = k_pool[untouched].clone(), v_pool[untouched].clone()
     kv_c, kv_p = prob.kv_len_t.clone(), prob.kv_len_t.clone()
@@ -188,8 +200,14 @@ def test_paged_commit_then_attention(name, ps):
     h_p = rd.rd_commit_accepted_paged(un, best, nacc, prob.k_new, prob.v_new, k_pool, v_pool, table, kv_p,
                                       prob.hidden)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(kv_p.cpu().numpy(), want["kv_len"])
+    np.testing.assert_array_equal(to_np(k_pool), want["k_pages"])
+    np.testing.assert_array_equal(to_np(v_pool), want["v_pages"])
+    for b in np.nonzero(want["committed"])[0]:
+        np.testing.assert_array_equal(to_np(h_p[b]), want["hidden_next"][b])
     assert torch.equal(kv_p, kv_c)
     moved = (kv_c != prob.kv_len_t).cpu().numpy()
+    np.testing.assert_array_equal(moved, want["committed"])
     assert moved[0] and not moved[-1]
     for b in np.nonzero(moved)[0]:
         assert torch.equal(h_p[b], h_c[b])
@@ -205,3 +223,37 @@ def test_paged_commit_then_attention(name, ps):
     torch.cuda.synchronize()
     assert torch.equal(a_p, a_c)
     say(f"[paged] commit {name} ps={ps}: {int(moved.sum())}/{cfg.B} committed, exact")
+
+
+@pytest.mark.parametrize("bad", [-1, 1 << 20])
+def test_paged_commit_with_a_table_entry_outside_the_pool(bad):
+    """A request whose committed positions reach an entry naming no page stays unchanged (no page written,
+    kv_len kept); the other requests commit as the oracle says."""
+    cfg = get_config("llama_mha").with_(B=4, S=256)
+    kv = np.array([60, 100, 0, 130], np.int32)
+    prob = Problem(cfg, base_seed(cfg, 6), plant=True, kv_len=kv)
+    res = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t,
+                         prob.hidden, prob.weight, want_logits=False)
+    acc = prob.oracle_accept(prob.oracle_target())
+    for key in ("best_beam", "accept_len"):
+        np.testing.assert_array_equal(res[key].cpu().numpy(), acc[key], err_msg=key)
+    k_pool, v_pool, table = make_pool(prob.k_cache, prob.v_cache, prob.kv_len_t, 64, seed=9,
+                                      unread_to_minus_one=False)
+    tbl = table.cpu().numpy()
+    tbl[0, 1] = bad      # request 0 commits positions 60..60+n: position 64 onwards has no page when n >= 4
+    tbl[1, 2] = bad      # request 1 commits 100..100+n (page 1): this entry is never reached
+    tbl[3, 2] = bad      # request 3 commits 130..130+n (page 2): always rejected
+    table = torch.from_numpy(tbl).to(k_pool.device)
+    want = oracle.commit_accepted_paged(prob.k_unp, prob.v_unp, prob.h_unp, acc["best_beam"], acc["accept_len"],
+                                        to_np(k_pool), to_np(v_pool), tbl, prob.kv_len)
+    kv_p = prob.kv_len_t.clone()
+    h_p = rd.rd_commit_accepted_paged(res["pack"]["unpacker"], res["best_beam"], res["accept_len"], prob.k_new,
+                                      prob.v_new, k_pool, v_pool, table, kv_p, prob.hidden)
+    torch.cuda.synchronize()
+    assert not want["committed"][3] and want["committed"][1] and want["committed"][2]
+    np.testing.assert_array_equal(kv_p.cpu().numpy(), want["kv_len"])
+    np.testing.assert_array_equal(to_np(k_pool), want["k_pages"])
+    np.testing.assert_array_equal(to_np(v_pool), want["v_pages"])
+    for b in np.nonzero(want["committed"])[0]:
+        np.testing.assert_array_equal(to_np(h_p[b]), want["hidden_next"][b])
+    say(f"[paged] commit with entry {bad}: committed {want['committed'].tolist()}, exact")

@@ -5,7 +5,6 @@ match lengths, best beam, accept length, accepted tokens) must match
 bit-exactly.  Floats are compared per row with the normwise error
 max|x - r| / max|r| <= 1e-5 (fp32) or 2e-2 (bf16).
 """
-import os
 import sys
 
 import numpy as np
@@ -146,21 +145,17 @@ def test_unpack_gather(dtype, X):
 
 # -------------------------------------------------------------------- attention
 def run_attention(prob: Problem, splits=None):
-    old = os.environ.get("RD_ATTN_SPLITS")
-    if splits is not None:
-        os.environ["RD_ATTN_SPLITS"] = str(splits)
+    old = rd.rd_set_knob(rd.RD_KNOB_ATTN_SPLITS, splits or 0)
     try:
         pk = rd.rd_pack_beams(prob.beams_t)
         mask = rd.rd_tree_mask(pk["unpacker"], pk["length"])
+        torch.cuda.synchronize()
+        prob.assert_pack_matches(pk, mask)
         out = rd.rd_tree_attention(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.kv_len_t,
                                    mask, pk["length"])
         torch.cuda.synchronize()
     finally:
-        if splits is not None:
-            if old is None:
-                os.environ.pop("RD_ATTN_SPLITS", None)
-            else:
-                os.environ["RD_ATTN_SPLITS"] = old
+        rd.rd_set_knob(rd.RD_KNOB_ATTN_SPLITS, old)
     return to_np(out)
 
 

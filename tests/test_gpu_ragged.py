@@ -2,8 +2,10 @@
 
 rd_pack_beams_mask_ragged and rd_unpack_accept_ragged against the oracle's
 ragged pack, mask, unpack and greedy accept, bit-exactly; full widths must
-reproduce the plain calls; and a whole ragged verification step must accept
-what the oracle accepts from the step's own target choices.
+reproduce the plain calls; and a whole ragged verification step must match
+the oracle alone: its pack and mask on every request, and on the checked
+requests its attention (per-beam definition), its greedy targets (fp64
+logits with enforced margins) and the accept that follows from them.
 """
 import sys
 
@@ -14,7 +16,7 @@ import torch
 import oracle
 import tree_attention_verification_rd_amd as rd
 from synthetic import get_config, base_seed, draw_beams
-from harness import mask_words_np
+from harness import Problem, TOL, mask_words_np, normwise_rows, to_np, fmt_err
 
 pytestmark = pytest.mark.gpu
 
@@ -93,42 +95,51 @@ def test_full_widths_reproduce_the_plain_calls():
 
 
 def test_ragged_verify_step_end_to_end():
-    """A ragged llama_mha-shaped step: the accept equals the oracle's on the step's own target choices."""
+    """A ragged llama_mha-shaped step against the oracle alone: pack and mask on every request;
+    attention, greedy targets and the accept on checked requests with planted acceptance."""
     cfg = get_config("llama_mha")
     rng = np.random.default_rng(7)
-    beams_np = draw_beams(cfg, base_seed(cfg, 5))
     B, W, L, P = cfg.B, cfg.W, cfg.L, cfg.P_max
     bw, bl = ragged_widths(rng, B, W, L)
-    dev = torch.device("cuda")
-    g = torch.Generator(device=dev)
-    g.manual_seed(11)
-
-    def rn(shape, scale=1.0):
-        return (torch.randn(shape, generator=g, device=dev) * scale).to(torch.bfloat16)
-
-    q, kn, vn = rn((B, P, cfg.Hq, cfg.D)), rn((B, P, cfg.Hkv, cfg.D)), rn((B, P, cfg.Hkv, cfg.D))
-    kc, vc = rn((B, cfg.Hkv, cfg.S, cfg.D)), rn((B, cfg.Hkv, cfg.S, cfg.D))
-    hidden = rn((B, P, cfg.hidden))
-    weight = rn((cfg.V, cfg.hidden), 0.02)
-    kv_len = torch.full((B,), cfg.S, dtype=torch.int32, device=dev)
-    res = rd.verify_step(dev_int(beams_np), q, kn, vn, kc, vc, kv_len, hidden, weight, want_logits=True,
+    checked = [0, 1, 2, 3, 5, B - 1]
+    prob = Problem(cfg, base_seed(cfg, 5), checked=checked, plant=True, beam_width=bw, beam_len=bl)
+    say(f"[ragged] step: widths {bw.tolist()} lengths {bl.tolist()}")
+    res = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache,
+                         prob.kv_len_t, prob.hidden, prob.weight, want_logits=True,
                          beam_width=dev_int(bw), beam_len=dev_int(bl))
     torch.cuda.synchronize()
-    ref = oracle.pack_beams(beams_np, bw, bl)
-    for key in ("tokens", "length", "unpacker"):
-        np.testing.assert_array_equal(res["pack"][key].cpu().numpy(), ref[key], err_msg=key)
+    prob.assert_pack_matches(res["pack"], res["mask"])
+    ref = prob.pack
     am = res["argmax"].cpu().numpy()
     assert (am[np.arange(P)[None, :] >= ref["length"][:, None]] == -1).all()
-    un = ref["unpacker"].reshape(B, -1)
-    target = np.take_along_axis(am, np.maximum(un, 0), axis=1).reshape(B, W, L)
-    acc = oracle.greedy_accept(beams_np, target, bw, bl)
+    # the oracle's own greedy targets, attention and accept on the checked requests
+    logits_ref = prob.oracle_logits()
+    target = oracle.argmax_first(logits_ref)
+    acc = prob.oracle_accept(target)
+    attn_ref = prob.oracle_attention()
+    attn = to_np(res["attn"])
+    logits = to_np(res["logits"])
+    bw_c = np.clip(bw, 0, W)
+    bl_c = np.clip(bl, 0, L)
+    errs, lerrs = [], []
+    for i, b in enumerate(checked):
+        for w in range(int(bw_c[b])):
+            for l in range(int(bl_c[b])):
+                slot = int(ref["unpacker"][b, w, l])
+                assert am[b, slot] == target[i, w, l], f"argmax b={b} w={w} l={l}"
+                errs.append(normwise_rows(attn[b, slot], attn_ref[i, w, l]))
+                lerrs.append(normwise_rows(logits[b, slot], logits_ref[i, w, l]))
+    errs, lerrs = np.asarray(errs), np.asarray(lerrs)
+    say(f"[ragged] step: attention normwise {fmt_err(errs)}, logits {fmt_err(lerrs)}")
+    assert errs.max() <= TOL[cfg.dtype] and lerrs.max() <= TOL[cfg.dtype]
     for key in ("match_len", "best_beam", "accept_len", "accepted_tokens"):
-        np.testing.assert_array_equal(res[key].cpu().numpy(), acc[key], err_msg=key)
+        np.testing.assert_array_equal(res[key].cpu().numpy()[checked], acc[key], err_msg=key)
+    assert acc["accept_len"].max() > 0
+    # padding candidates unpack to zero rows, valid ones carry their slot's logits
     unp = res["unpacked"]
-    pad = torch.from_numpy(ref["unpacker"] < 0).to(dev)
+    pad = torch.from_numpy(ref["unpacker"] < 0).to(unp.device)
     assert (unp[pad] == 0).all()
-    # valid candidates carry their slot's logits
     for b in range(B):
-        for w in range(int(min(max(bw[b], 0), W))):
-            for l in range(int(min(max(bl[b], 0), L))):
+        for w in range(int(bw_c[b])):
+            for l in range(int(bl_c[b])):
                 assert torch.equal(unp[b, w, l], res["logits"][b, ref["unpacker"][b, w, l]])

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     lib = rd.load_library()
     for code, word in ((0, b"RD_OK"), (-1, b"RD_E_ARG"), (-2, b"RD_E_UNSUPPORTED"), (-3, b"RD_E_WORKSPACE"),
-                       (-4, b"RD_E_HIP")):
+                       (-4, b"RD_E_HIP"), (-5, b"RD_E_CONTENT")):
         assert lib.rd_status_string(code).startswith(word)
     assert lib.rd_version() >= 100
 
@@ -119,3 +119,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(rd, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         rd.load_library()
+
+
+def test_knobs_and_debug_switch():
+    """Knobs take non-negative values for the three known knobs and return the previous value;
+    the debug switch returns its previous setting.  Neither touches the device."""
+    lib = rd.load_library()
+    for knob in (rd.RD_KNOB_ATTN_SPLITS, rd.RD_KNOB_ATTN_FEWROW, rd.RD_KNOB_LM_SHAPE):
+        assert lib.rd_set_knob(knob, 3) == 0
+        assert lib.rd_set_knob(knob, 0) == 3
+    assert lib.rd_set_knob(0, 1) == -1
+    assert lib.rd_set_knob(4, 1) == -1
+    assert lib.rd_set_knob(rd.RD_KNOB_ATTN_SPLITS, -2) == -1
+    prev = lib.rd_set_debug(1)
+    assert lib.rd_set_debug(0) == 1
+    lib.rd_set_debug(prev)
+    # debug mode only adds device-side checks: host validation still comes first, without a device
+    lib.rd_set_debug(1)
+    try:
+        fake = ctypes.c_void_p(0x1000)
+        assert lib.rd_tree_mask(None, None, 2, -3, 4, None, None) == -1
+        assert lib.rd_pack_beams(fake, 2, 65, 4, fake, fake, fake, None, None, None) == -2
+    finally:
+        lib.rd_set_debug(prev)

@@ -19,11 +19,13 @@ __all__ = [
     "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_pack_beams_mask_ragged", "rd_tree_attention",
     "rd_tree_attention_paged", "rd_unpack_accept_ragged", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "rd_stochastic_accept",
-    "rd_stochastic_accept_workspace_size", "verify_step",
+    "rd_stochastic_accept_workspace_size", "verify_step", "rd_set_knob", "rd_set_debug",
+    "RD_KNOB_ATTN_SPLITS", "RD_KNOB_ATTN_FEWROW", "RD_KNOB_LM_SHAPE",
     "VerifyBuffers",
 ]
 
-RD_OK, RD_E_ARG, RD_E_UNSUPPORTED, RD_E_WORKSPACE, RD_E_HIP = 0, -1, -2, -3, -4
+RD_OK, RD_E_ARG, RD_E_UNSUPPORTED, RD_E_WORKSPACE, RD_E_HIP, RD_E_CONTENT = 0, -1, -2, -3, -4, -5
+RD_KNOB_ATTN_SPLITS, RD_KNOB_ATTN_FEWROW, RD_KNOB_LM_SHAPE = 1, 2, 3
 RD_F32, RD_BF16 = 0, 1
 MAX_BEAMS, MAX_BEAM_LEN = 64, 16
 
@@ -32,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "rd_pack_beams_mask_ragged", "rd_unpack_accept_ragged",
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
-    "rd_stochastic_accept_workspace_size", "rd_stochastic_accept",
+    "rd_stochastic_accept_workspace_size", "rd_stochastic_accept", "rd_set_knob", "rd_set_debug",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +65,8 @@ def load_library():
     sigs = {
         "rd_status_string": ([i32], ctypes.c_char_p),
         "rd_version": ([], i32),
+        "rd_set_knob": ([i32, i32], i32),
+        "rd_set_debug": ([i32], i32),
         "rd_pack_beams": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
         "rd_tree_mask": ([vp, vp, i32, i32, i32, vp, vp], i32),
         "rd_pack_beams_mask": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp], i32),
@@ -136,6 +140,18 @@ def _out(t, name, shape, dtype, device):
 
 
 # -------------------------------------------------------------- entry points
+def rd_set_knob(knob: int, value: int) -> int:
+    """Force a tuning choice (RD_KNOB_*; 0 = automatic).  Returns the previous value."""
+    code = load_library().rd_set_knob(int(knob), int(value))
+    _check(min(code, 0), "rd_set_knob")
+    return code
+
+
+def rd_set_debug(on: bool) -> bool:
+    """Switch the library's debug-mode content checks on or off.  Returns the previous setting."""
+    return bool(load_library().rd_set_debug(1 if on else 0))
+
+
 def rd_pack_beams(beams: torch.Tensor, *, packed_tokens=None, packed_len=None, unpacker=None,
                   packed_depth=None, packed_src=None, with_depth_src: bool = True) -> dict:
     """Step 1: pack beams [B,W,L] int32 into the deduplicated token tree."""

@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/rd.h"
@@ -34,6 +35,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? RD_OK : RD_E_HIP; }
 bool beam_shape_ok(int B, int W, int L) { return B >= 0 && W >= 0 && L >= 0; }
 bool beam_shape_supported(int W, int L) { return W <= rd::kMaxBeams && L <= rd::kMaxBeamLen; }
 
+// Debug mode: check the device-side values a call trusts before it launches anything.
+int debug_check(rd_stream_t stream, std::initializer_list<rd::RangeCheck> checks,
+                const rd::TableCheck *table = nullptr) {
+    if (!rd::debug_checks()) return RD_OK;
+    return rd::check_contents(as_stream(stream), checks.begin(), static_cast<int>(checks.size()), table);
+}
+
 }  // namespace
 
 extern "C" {
@@ -45,6 +53,7 @@ const char *rd_status_string(int status) {
         case RD_E_UNSUPPORTED: return "RD_E_UNSUPPORTED: size or dtype outside the library's limits";
         case RD_E_WORKSPACE: return "RD_E_WORKSPACE: workspace smaller than the size query returned";
         case RD_E_HIP: return "RD_E_HIP: a HIP launch failed";
+        case RD_E_CONTENT: return "RD_E_CONTENT: a device-side length, slot or page id is out of range (debug mode)";
         default: return "unknown rd status";
     }
 }
@@ -89,6 +98,9 @@ int rd_tree_mask(const int32_t *unpacker, const int32_t *packed_len, int B, int 
     if (B == 0 || W == 0 || L == 0) return RD_OK;
     if (!unpacker || !packed_len || !mask) return RD_E_ARG;
     if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    const int P = W * L;
+    const int dbg = debug_check(stream, {{unpacker, static_cast<int64_t>(B) * P, -1, P}, {packed_len, B, 0, P + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_tree_mask(unpacker, packed_len, B, W, L, mask, as_stream(stream)));
 }
 
@@ -124,6 +136,8 @@ int rd_tree_attention(int dtype, const void *q, const void *k_new, const void *v
     if (!(scale >= 0.f) || !(scale <= 3.4e38f)) return RD_E_ARG;  // finite, non-negative (rejects NaN)
     const rd::AttnPlan plan = rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, S_max);
     if (ws_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && !ws)) return RD_E_WORKSPACE;
+    const int dbg = debug_check(stream, {{kv_len, B, 0, S_max + 1}, {packed_len, B, 0, P_max + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_attention(dtype, plan, q, k_new, v_new, k_cache, v_cache, kv_len, mask, packed_len,
                                            B, P_max, Hq, Hkv, D, S_max, scale, out, ws, as_stream(stream)));
 }
@@ -146,6 +160,10 @@ int rd_tree_attention_paged(int dtype, const void *q, const void *k_new, const v
     const rd::AttnPlan plan = rd::plan_attention(dtype, B, P_max, Hq, Hkv, D, static_cast<int>(S));
     if (ws_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && !ws)) return RD_E_WORKSPACE;
     const rd::PagedKV pk{block_table, max_pages, page_size, num_pages > 0 ? num_pages : 1};
+    const rd::TableCheck tc{block_table, kv_len, B, max_pages, page_size, num_pages};
+    const int dbg = debug_check(stream, {{kv_len, B, 0, static_cast<int>(S) + 1}, {packed_len, B, 0, P_max + 1}},
+                                S > 0 ? &tc : nullptr);
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_attention(dtype, plan, q, k_new, v_new, k_pages, v_pages, kv_len, mask, packed_len,
                                            B, P_max, Hq, Hkv, D, static_cast<int>(S), scale, out, ws,
                                            as_stream(stream), &pk));
@@ -178,6 +196,8 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, 
     if (!hidden || !weight || !argmax) return RD_E_ARG;
     const rd::LmPlan plan = rd::plan_lm_head(dtype, B, P_max, K, V);
     if (ws_bytes < plan.ws_bytes || !ws) return RD_E_WORKSPACE;
+    const int dbg = debug_check(stream, {{packed_len, packed_len ? B : 0, 0, P_max + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P_max, K, V, logits, argmax,
                                          ws, as_stream(stream)));
 }
@@ -204,6 +224,8 @@ int unpack_accept(const int32_t *beams, const int32_t *bwid, const int32_t *blen
         const int64_t chunks = (row_bytes + 1023) / 1024;  // upper bound on blocks per row
         if (rows * chunks * 256 >= (1LL << 32)) return RD_E_UNSUPPORTED;
     }
+    const int dbg = debug_check(stream, {{unpacker, static_cast<int64_t>(B) * W * L, -1, W * L}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_unpack_accept(row_bytes ? packed : nullptr, row_bytes ? unpacked : nullptr, unpacker,
                                                row_bytes, beams, packed_argmax, B, W, L, match_len, best_beam,
                                                accept_len, accepted_tokens, s, bwid, blen));
@@ -246,6 +268,9 @@ int rd_stochastic_accept(int dtype, const int32_t *unpacker, const int32_t *pack
     if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
     if (dtype != RD_F32 && dtype != RD_BF16) return RD_E_UNSUPPORTED;
     if (ws_bytes < rd::stochastic_workspace_bytes(B, W, L) || !ws) return RD_E_WORKSPACE;
+    const int dbg = debug_check(stream, {{unpacker, static_cast<int64_t>(B) * W * L, -1, W * L},
+                                         {packed_len, B, 0, W * L + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_stochastic_accept(dtype, unpacker, packed_len, packed_tokens, logits, q, u_accept,
                                                    u_bonus, B, W, L, V, best_beam, accept_len, accepted_tokens, path,
                                                    ws, as_stream(stream)));
@@ -266,6 +291,9 @@ int rd_commit_accepted(int dtype, const int32_t *unpacker, const int32_t *best_b
     // copy units (2 bytes at the narrowest) of one request must index in 32 bits
     const int64_t units = (2 * static_cast<int64_t>(Hkv) * L * D + (hidden ? K : 0)) * esize / 2;
     if (units >= (1LL << 30)) return RD_E_UNSUPPORTED;
+    const int dbg = debug_check(stream, {{unpacker, static_cast<int64_t>(B) * W * L, -1, W * L},
+                                         {kv_len, B, 0, S_max + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_commit(static_cast<int>(esize), unpacker, best_beam, accept_len, k_new, v_new,
                                         hidden, B, W, L, Hkv, D, K, S_max, k_cache, v_cache, kv_len, hidden_next,
                                         as_stream(stream)));
@@ -291,6 +319,9 @@ int rd_commit_accepted_paged(int dtype, const int32_t *unpacker, const int32_t *
     const int64_t units = (2 * static_cast<int64_t>(Hkv) * L * D + (hidden ? K : 0)) * esize / 2;
     if (units >= (1LL << 30)) return RD_E_UNSUPPORTED;
     const rd::PagedKV pk{block_table, max_pages, page_size, num_pages};
+    const int dbg = debug_check(stream, {{unpacker, static_cast<int64_t>(B) * W * L, -1, W * L},
+                                         {kv_len, B, 0, static_cast<int>(S) + 1}});
+    if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_commit(static_cast<int>(esize), unpacker, best_beam, accept_len, k_new, v_new,
                                         hidden, B, W, L, Hkv, D, K, static_cast<int>(S), k_pages, v_pages, kv_len,
                                         hidden_next, as_stream(stream), &pk));

@@ -29,10 +29,10 @@
 // the log2 domain.  With more than one split, each split writes (max, sum,
 // unnormalised O) in fp32 and a combine kernel merges them.
 #include <math.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
+#include "../../include/rd.h"
 #include "rd_common.h"
 #include "rd_internal.h"
 
@@ -678,11 +678,6 @@ __global__ __launch_bounds__(64) void k_tree_attn_f32(const float *__restrict__ 
     }
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
-
 }  // namespace
 
 AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int S_max) {
@@ -699,7 +694,7 @@ AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int
     plan.qpw = 2;
     plan.nwave = rows <= 128 ? 4 : 8;
     plan.ksplit = rows <= 64 ? 2 : 1;
-    if (rows <= 64 && env_int("RD_ATTN_FEWROW", 1) == 1) {
+    if (rows <= 64 && knob(RD_KNOB_ATTN_FEWROW) != 2) {
         // (1, 8, 2) with lane-interleaved rows: four query groups of ~rows/4
         plan.qpw = 1;
         plan.nwave = 8;
@@ -715,7 +710,7 @@ AttnPlan plan_attention(int dtype, int B, int P_max, int Hq, int Hkv, int D, int
     const long target = device_cu_count();
     int nsplit = static_cast<int>((target + units - 1) / units);
     nsplit = min(nsplit, max(1, tiles / 8));
-    nsplit = env_int("RD_ATTN_SPLITS", nsplit);
+    if (knob(RD_KNOB_ATTN_SPLITS) > 0) nsplit = knob(RD_KNOB_ATTN_SPLITS);
     nsplit = max(1, min(nsplit, min(max(tiles, 1), kMaxSplits)));
     const int chunk_tiles = (max(tiles, 1) + nsplit - 1) / nsplit;
     plan.nsplit = (max(tiles, 1) + chunk_tiles - 1) / chunk_tiles;

@@ -32,21 +32,33 @@ struct CommitArgs {
 // once by thread 0 after the copies, so it can be advanced in place within
 // the one launch.
 // With PAGED, position t goes to row t % page_size of page
-// block_table[b, t / page_size] (clamped into the pool).
+// block_table[b, t / page_size].  Every page id the request would write is
+// checked first: one that names no page of the pool (negative or past it)
+// leaves the whole request unchanged, like an overflow, so a write never
+// lands in a page the request does not own.
 template <typename T, int U, bool PAGED>
 __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
     __shared__ int slot[kMaxBeamLen];
+    __shared__ int pages[kMaxBeamLen];
     const int b = blockIdx.x;
     const int w = a.best_beam[b];
     const int n = a.accept_len[b];
     const int c = a.kv_len[b];
-    const bool ok = w >= 0 && w < a.W && n >= 0 && n < a.L && c >= 0 && c <= a.S - (n + 1);
+    const bool fits = w >= 0 && w < a.W && n >= 0 && n < a.L && c >= 0 && c <= a.S - (n + 1);
     const int rows = n + 1;
-    if (ok && static_cast<int>(threadIdx.x) < rows) {
+    int mine = 1;  // this thread's position has a page (or needs none)
+    if (fits && static_cast<int>(threadIdx.x) < rows) {
         const int s = a.unpacker[(static_cast<size_t>(b) * a.W + w) * a.L + threadIdx.x];
         slot[threadIdx.x] = min(max(s, 0), a.P - 1);
+        if constexpr (PAGED) {
+            // c + rows <= S = max_pages * page_size, so the table index is in range
+            const int t = c + static_cast<int>(threadIdx.x);
+            const int32_t pg = a.bt[static_cast<size_t>(b) * a.max_pages + t / a.page_size];
+            pages[threadIdx.x] = pg;
+            mine = (pg >= 0 && static_cast<int64_t>(pg) < a.num_pages) ? 1 : 0;
+        }
     }
-    __syncthreads();
+    const bool ok = __syncthreads_and(mine) && fits;
     if (!ok) return;
 
     const int per_head = rows * a.row_units;
@@ -77,11 +89,7 @@ __global__ __launch_bounds__(1024) void k_commit(CommitArgs a) {
         size_t drow;
         if constexpr (PAGED) {
             const int t = c + j;
-            const int64_t pg = min(max(static_cast<int64_t>(a.bt[static_cast<size_t>(b) * a.max_pages +
-                                                                 t / a.page_size]),
-                                       static_cast<int64_t>(0)),
-                                   a.num_pages - 1);
-            drow = (static_cast<size_t>(pg) * a.Hkv + g) * a.page_size + t % a.page_size;
+            drow = (static_cast<size_t>(pages[j]) * a.Hkv + g) * a.page_size + t % a.page_size;
         } else {
             drow = (static_cast<size_t>(b) * a.Hkv + g) * a.S + c + j;
         }

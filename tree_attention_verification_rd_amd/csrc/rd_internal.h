@@ -81,4 +81,23 @@ hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const in
 
 int device_cu_count();
 
+// tuning knobs (rd_set_knob): 0 = automatic
+int knob(int which);
+int set_knob(int which, int value);
+// debug mode (rd_set_debug / RD_DEBUG): device-side contents are checked before launching
+bool debug_checks();
+int set_debug(int on);
+struct RangeCheck {  // p[0..n) must lie in [lo, hi)
+    const int32_t *p;
+    int64_t n;
+    int lo, hi;
+};
+struct TableCheck {  // block-table entries of positions below kv_len[b] must lie in [0, num_pages)
+    const int32_t *bt, *kv_len;
+    int B, max_pages, page_size;
+    int64_t num_pages;
+};
+// runs the checks on `stream` and waits for them: RD_OK, RD_E_CONTENT or RD_E_HIP
+int check_contents(hipStream_t stream, const RangeCheck *checks, int n, const TableCheck *table = nullptr);
+
 }  // namespace rd

@@ -21,10 +21,10 @@
 // partial per (row, vocabulary tile); a second kernel reduces the partials
 // in a fixed order.
 #include <math.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
+#include "../../include/rd.h"
 #include "rd_common.h"
 #include "rd_internal.h"
 
@@ -562,9 +562,9 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
         // stages: gqa 1590 vs 1675 us, long_ctx 473 vs 522, dedup_p0.5
         // 6938 vs 7144).  (Ring depths measured on MI355X: deeper weight
         // rings slow the few-row shape.)
-        // RD_LM_VARIANT forces one.
-        const char *env = getenv("RD_LM_VARIANT");
-        plan.variant = (env && *env) ? (atoi(env) != 0) : (plan.rows_pad > 512 ? 1 : 0);
+        // The RD_KNOB_LM_SHAPE knob forces one.
+        const int forced = knob(RD_KNOB_LM_SHAPE);
+        plan.variant = forced == 1 ? 0 : forced == 2 ? 1 : (plan.rows_pad > 512 ? 1 : 0);
         plan.vtile = plan.variant ? 256 : 128;
         plan.rtile = 256;
     }
