@@ -67,7 +67,8 @@ enum rd_status_code {
     RD_E_UNSUPPORTED = -2,
     RD_E_WORKSPACE = -3,
     RD_E_HIP = -4,
-    RD_E_CONTENT = -5  /* debug mode only: a device-side value is out of range */
+    RD_E_CONTENT = -5, /* debug mode only: a device-side value is out of range */
+    RD_E_SCRATCH = -6  /* rd_lm_head_argmax_noalloc: sizes need more than its fixed scratch */
 };
 
 enum rd_dtype {
@@ -260,6 +261,29 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len,
                       const void *weight, int B, int P_max, int K, int V,
                       void *logits, int32_t *argmax, void *ws, size_t ws_bytes,
                       rd_stream_t stream);
+
+/*
+ * rd_lm_head_argmax for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and limits as rd_lm_head_argmax, but
+ * no workspace: the argmax partials go to a fixed array of
+ * RD_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every
+ * device it runs on, for the life of the process.  The call allocates
+ * nothing and frees nothing.
+ *   - RD_E_SCRATCH when rd_lm_head_workspace_size(dtype, B, P_max, K, V)
+ *     exceeds RD_NOALLOC_SCRATCH_BYTES (nothing is launched).  32 MiB holds
+ *     e.g. B*P_max = 32768 rows at V = 32000, or 4096 rows at V = 128256.
+ *   - Every call on one device shares that device's array and leaves its
+ *     contents behind; the kernels overwrite every partial they read, so
+ *     nothing needs clearing.  Calls that overlap on one device (two
+ *     streams, or two host threads) race on the array: serialise them.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current.
+ */
+#define RD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int rd_lm_head_argmax_noalloc(int dtype, const void *hidden, const int32_t *packed_len,
+                              const void *weight, int B, int P_max, int K, int V,
+                              void *logits, int32_t *argmax, rd_stream_t stream);
 
 /*
  * Steps 3b and 4 -- unpack and greedy accept.

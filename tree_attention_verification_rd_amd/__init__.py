@@ -19,12 +19,13 @@ __all__ = [
     "rd_pack_beams", "rd_tree_mask", "rd_pack_beams_mask", "rd_pack_beams_mask_ragged", "rd_tree_attention",
     "rd_tree_attention_paged", "rd_unpack_accept_ragged", "rd_tree_attention_workspace_size",
     "rd_lm_head_argmax", "rd_lm_head_workspace_size", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged", "rd_stochastic_accept",
-    "rd_stochastic_accept_workspace_size", "verify_step", "rd_set_knob", "rd_set_debug",
+    "rd_stochastic_accept_workspace_size", "verify_step", "rd_set_knob", "rd_set_debug", "rd_lm_head_argmax_noalloc",
     "RD_KNOB_ATTN_SPLITS", "RD_KNOB_ATTN_FEWROW", "RD_KNOB_LM_SHAPE",
     "VerifyBuffers",
 ]
 
-RD_OK, RD_E_ARG, RD_E_UNSUPPORTED, RD_E_WORKSPACE, RD_E_HIP, RD_E_CONTENT = 0, -1, -2, -3, -4, -5
+RD_OK, RD_E_ARG, RD_E_UNSUPPORTED, RD_E_WORKSPACE, RD_E_HIP, RD_E_CONTENT, RD_E_SCRATCH = 0, -1, -2, -3, -4, -5, -6
+RD_NOALLOC_SCRATCH_BYTES = 32 << 20
 RD_KNOB_ATTN_SPLITS, RD_KNOB_ATTN_FEWROW, RD_KNOB_LM_SHAPE = 1, 2, 3
 RD_F32, RD_BF16 = 0, 1
 MAX_BEAMS, MAX_BEAM_LEN = 64, 16
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "rd_tree_attention_workspace_size", "rd_tree_attention", "rd_tree_attention_paged", "rd_lm_head_workspace_size",
     "rd_lm_head_argmax", "rd_unpack_accept", "rd_commit_accepted", "rd_commit_accepted_paged",
     "rd_stochastic_accept_workspace_size", "rd_stochastic_accept", "rd_set_knob", "rd_set_debug",
+    "rd_lm_head_argmax_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +81,7 @@ def load_library():
                                      f32, vp, vp, sz, vp], i32),
         "rd_lm_head_workspace_size": ([i32, i32, i32, i32, i32], sz),
         "rd_lm_head_argmax": ([i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp], i32),
+        "rd_lm_head_argmax_noalloc": ([i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp], i32),
         "rd_unpack_accept": ([vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp], i32),
         "rd_commit_accepted": ([i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                 vp], i32),
@@ -324,6 +327,27 @@ def rd_lm_head_argmax(hidden, packed_len, weight, *, want_logits: bool = True, l
     _need(workspace, "workspace", torch.uint8, None, dev)
     _check(lib.rd_lm_head_argmax(dt, _p(hidden), _p(packed_len), _p(weight), B, P, K, V, _p(logits), _p(argmax),
                                  _p(workspace), workspace.numel(), _stream(hidden)), "rd_lm_head_argmax")
+    return logits, argmax
+
+
+def rd_lm_head_argmax_noalloc(hidden, packed_len, weight, *, logits, argmax):
+    """rd_lm_head_argmax without a workspace: the library's fixed device scratch holds the argmax
+    partials.  The caller supplies every output (logits may be None); nothing is allocated here or in
+    the library.  Raises RdError(RD_E_SCRATCH) when the sizes need more than RD_NOALLOC_SCRATCH_BYTES."""
+    lib = load_library()
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden", hidden.dtype)
+    B, P, K = hidden.shape
+    dev = hidden.device
+    V = weight.shape[0]
+    _need(weight, "weight", hidden.dtype, (V, K), dev)
+    if packed_len is not None:
+        _need(packed_len, "packed_len", torch.int32, (B,), dev)
+    if logits is not None:
+        _need(logits, "logits", hidden.dtype, (B, P, V), dev)
+    _need(argmax, "argmax", torch.int32, (B, P), dev)
+    _check(lib.rd_lm_head_argmax_noalloc(dt, _p(hidden), _p(packed_len), _p(weight), B, P, K, V, _p(logits),
+                                         _p(argmax), _stream(hidden)), "rd_lm_head_argmax_noalloc")
     return logits, argmax
 
 

@@ -54,6 +54,9 @@ const char *rd_status_string(int status) {
         case RD_E_WORKSPACE: return "RD_E_WORKSPACE: workspace smaller than the size query returned";
         case RD_E_HIP: return "RD_E_HIP: a HIP launch failed";
         case RD_E_CONTENT: return "RD_E_CONTENT: a device-side length, slot or page id is out of range (debug mode)";
+        case RD_E_SCRATCH:
+            return "RD_E_SCRATCH: the call needs more scratch than the fixed device array holds "
+                   "(RD_NOALLOC_SCRATCH_BYTES); use the workspace entry point";
         default: return "unknown rd status";
     }
 }
@@ -196,6 +199,22 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, 
     if (!hidden || !weight || !argmax) return RD_E_ARG;
     const rd::LmPlan plan = rd::plan_lm_head(dtype, B, P_max, K, V);
     if (ws_bytes < plan.ws_bytes || !ws) return RD_E_WORKSPACE;
+    const int dbg = debug_check(stream, {{packed_len, packed_len ? B : 0, 0, P_max + 1}});
+    if (dbg != RD_OK) return dbg;
+    return hip_status(rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P_max, K, V, logits, argmax,
+                                         ws, as_stream(stream)));
+}
+
+int rd_lm_head_argmax_noalloc(int dtype, const void *hidden, const int32_t *packed_len, const void *weight, int B,
+                              int P_max, int K, int V, void *logits, int32_t *argmax, rd_stream_t stream) {
+    const int chk = lm_check(dtype, B, P_max, K, V);
+    if (chk != RD_OK) return chk;
+    if (B == 0 || P_max == 0) return RD_OK;
+    if (!hidden || !weight || !argmax) return RD_E_ARG;
+    const rd::LmPlan plan = rd::plan_lm_head(dtype, B, P_max, K, V);
+    if (plan.ws_bytes > RD_NOALLOC_SCRATCH_BYTES) return RD_E_SCRATCH;
+    void *ws = nullptr;
+    if (rd::noalloc_scratch(&ws) != hipSuccess) return RD_E_HIP;
     const int dbg = debug_check(stream, {{packed_len, packed_len ? B : 0, 0, P_max + 1}});
     if (dbg != RD_OK) return dbg;
     return hip_status(rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P_max, K, V, logits, argmax,

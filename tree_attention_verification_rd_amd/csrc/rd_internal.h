@@ -58,6 +58,8 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V);
 hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, const int32_t *plen,
                           const void *weight, int B, int P_max, int K, int V, void *logits,
                           int32_t *argmax, void *ws, hipStream_t stream);
+// device address of the current device's fixed projection scratch (RD_NOALLOC_SCRATCH_BYTES)
+hipError_t noalloc_scratch(void **out);
 
 // unpack gather + accept
 hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,

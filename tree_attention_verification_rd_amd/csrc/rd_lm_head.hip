@@ -22,6 +22,7 @@
 // in a fixed order.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/rd.h"
@@ -31,6 +32,12 @@
 namespace rd {
 
 namespace {
+
+// Fixed device scratch of rd_lm_head_argmax_noalloc: the per-(row,
+// vocabulary tile) argmax partials live here instead of in a caller's
+// workspace.  Every device the library runs on holds its own copy for the
+// life of the process; calls on one device share it.
+static __device__ __align__(256) uint8_t scratch[RD_NOALLOC_SCRATCH_BYTES];
 
 
 struct LmArgs {
@@ -539,6 +546,29 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const float *__restrict__
 constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
+
+// Device address of this device's `scratch`.  The array's name is only a
+// host-side stand-in for it, so the address is looked up once per device
+// (with that device current) and kept; kernels receive it as an argument.
+hipError_t noalloc_scratch(void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
     LmPlan plan{};
