@@ -45,6 +45,7 @@ constexpr int kCombRows = 64;  // rows per combine workgroup
 constexpr int kMaxSplits = 64;
 constexpr int kMaxMaskWords = (kMaxBeams * kMaxBeamLen) / 32;
 constexpr float kRescale = 8.f;  // lazy-rescale threshold of the online softmax (log2 units)
+constexpr int kTileFull = 0, kTileMasked = 1;  // kinds of key tile
 
 struct AttnArgs {
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
@@ -87,6 +88,12 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4 *>(static_cast<uintptr_t>(addr)));
 }
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// the same read from an LDS byte pointer: a constant added to a common base
+// folds into the instruction's offset field instead of an address add
+__device__ __forceinline__ bf16x4 lds_read_tr16(const lds_u8 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_bf16x4 *>(const_cast<lds_u8 *>(p)));
+}
 
 // Rows of query block qi of query group q: blocked, rows row0 + (NQG*qi +
 // q)*16 + (0..15), or, with LI (lane-interleaved, for few rows), rows
@@ -118,11 +125,16 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t stage[NS * STAGEB];
     __shared__ uint32_t mwords[RB * kMaxMaskWords];  // tree-mask rows of this block's tokens
 
-    // row blocks are the slowest index: blocks with no valid rows (their
-    // count depends on the packed lengths) come last in dispatch order
-    const int L = a.B * a.Hkv * a.nsplit;
-    const int qb = blockIdx.x / L;
-    const int rest = blockIdx.x - qb * L;
+    // Row blocks are the slowest index: blocks with no valid rows (their
+    // count depends on the packed lengths) come last in dispatch order.
+    // Interleaving them with real blocks -- e.g. to run the two row blocks
+    // of one (request, KV head) side by side on one XCD so that the second
+    // cache read hits L2 -- measured up to 1.8x slower (gqa, dedup sweep at
+    // p = 0.9): the idle blocks' places in the dispatch order leave some
+    // shader engines with most of the real work.
+    const int L_ = a.B * a.Hkv * a.nsplit;
+    const int qb = blockIdx.x / L_;
+    const int rest = blockIdx.x - qb * L_;
     const int s = rest % a.nsplit;
     const int g = (rest / a.nsplit) % a.Hkv;
     const int b = rest / (a.nsplit * a.Hkv);
@@ -162,11 +174,10 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     const int c0 = s * a.chunk;
     const int c1 = min(c0 + a.chunk, kvl);
     const int ncache = (c1 > c0) ? (c1 - c0 + kBlockN - 1) / kBlockN : 0;
-    int tok_hi = 0, npk = 0;
-    if (s == a.nsplit - 1) {
-        tok_hi = (min(row0 + RB, Mb) - 1) / a.G + 1;
-        npk = (tok_hi + kBlockN - 1) / kBlockN;
-    }
+    // values the lambdas below read are const: a mutable local selected by
+    // reference in a lambda stays in scratch memory
+    const int tok_hi = (s == a.nsplit - 1) ? (min(row0 + RB, Mb) - 1) / a.G + 1 : 0;
+    const int npk = (tok_hi + kBlockN - 1) / kBlockN;
     const int ntile = ncache + npk;
     const int tok_lo = row0 / a.G;
     bf16x8 qf[QPW][NKC];
@@ -190,26 +201,37 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     // (the cache part of the softmax does not depend on key order; strided
     // tiles spread each load of a long cache over many HBM pages instead of
     // one 16 KB run, which measured faster there and slower elsewhere).  ic
-    // is rotated per block so that concurrent blocks, whose slabs sit at
-    // power-of-two strides, do not all address the same offsets.
-    const int trot = ncache > 0 ? (b * 7 + g * 3 + qb * 5) % ncache : 0;
+    // is rotated per (request, KV head) so that concurrent blocks, whose
+    // slabs sit at power-of-two strides, do not all address the same
+    // offsets; the row blocks of one (request, KV head) share the rotation.
     const int nck = c1 - c0;  // cache keys of this split
     const bool strided = !PAGED && a.nsplit > 1;
     const int kmul = strided ? ncache : 1;  // pos(j) = ic*kblk + kmul*j
     const int kblk = strided ? 1 : kBlockN;
+    // Tiles ic < nfull are full (every key before the split's end), the
+    // rest of the cache tiles partial.  The rotation runs over the full
+    // tiles only, so the partial ones come after them and the loop splits
+    // into a run of full tiles and a run of masked ones (partial cache tiles,
+    // then packed tiles).
+    const int nfull = strided ? min(max(nck - (kBlockN - 1) * ncache, 0), ncache) : nck / kBlockN;
+    const int trot = nfull > 0 ? (b * 7 + g * 3) % nfull : 0;  // the same for every row block
+    auto tile_ic = [=](int i) { return i < nfull ? (i + trot >= nfull ? i + trot - nfull : i + trot) : i; };
     // Load j = NWAVE*jj + wave of an operand covers tile keys KPL*j .. +KPL-1;
     // lane i stores LDS chunk slot i % KCH of key KPL*j + i / KCH, which
     // holds head-dim chunk slot ^ (key & 7).
     const int lkey = lane / KCH;
     const int lslot = lane % KCH;
-    auto issue_tile = [&](int i, int slot) {
+    const int c1v = c1;
+    // by value: a closure holding references to these locals kept them in
+    // scratch memory and selected between their addresses
+    auto issue_tile = [=](int i, int slot) {
         const bool cache = i < ncache;
         i32x4_t rk = cache ? rk_c : rk_n;
         i32x4_t rv = cache ? rv_c : rv_n;
-        const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
+        const int ic = tile_ic(i);
         const int kbase = cache ? c0 + ic * kblk : (i - ncache) * kBlockN;
         const int kstep = cache ? kmul : 1;
-        const int klim = (i >= ntile) ? 0 : (cache ? c1 : tok_hi);
+        const int klim = (i >= ntile) ? 0 : (cache ? c1v : tok_hi);
         const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
         const uint32_t kdst = lds0 + slot * STAGEB;
         int kres = 0;  // key at the resource base
@@ -263,10 +285,36 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     // One pass over this key group's part of tile i for query blocks
     // 0 .. NQ-1.  K fragments of a head-dim step are read one step ahead and
     // serve every block; scores stay unscaled (the scale folds into the
-    // exponent).
-    auto compute_tile = [&](int i, uint32_t sbase, auto nq_c) {
+    // exponent).  KIND is the tile's kind, known before the call: a full
+    // cache tile (no masking) or a masked one -- a partial cache tile (keys
+    // past the split's end) or a packed tile (tree mask).  A separate
+    // instance keeps the common full-tile path free of the masking code and
+    // of the register copies that merging the paths would need.
+    auto compute_tile = [&](int i, uint32_t sbase, auto nq_c, auto kind_c) {
         constexpr int NQ = decltype(nq_c)::value;
+        constexpr int KIND = decltype(kind_c)::value;
         const uint8_t *st = stage + (sbase - lds0);
+        const int wi = 2 * (i - ncache);
+        const bool packed = KIND == kTileMasked && i >= ncache;  // wave-uniform
+        uint32_t mw[NQ][2];  // this lane's row's mask words for the tile's two 32-key halves
+        if (packed) {
+            // A packed tile whose keys are invisible to every row of this
+            // wavefront's blocks changes no row's softmax state: skip it.
+            // Only ancestors are visible, so with a deep, narrow tree most
+            // packed tiles are invisible to a given block of 16 rows.
+            bool any = false;
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                // the second word exists unless the tile is the last and P_max <= 32*(2*tile+1);
+                // it is read from a clamped index and then dropped (a select of loaded
+                // values, not of addresses, which would put the operands in scratch)
+                const uint32_t w1 = mwords[lt[qi] * a.nw + min(wi + 1, a.nw - 1)];
+                mw[qi][0] = mwords[lt[qi] * a.nw + wi];
+                mw[qi][1] = (wi + 1 < a.nw) ? w1 : 0u;
+                any |= (KSPLIT == 2 ? (wk == 0 ? mw[qi][0] : mw[qi][1]) : (mw[qi][0] | mw[qi][1])) != 0u;
+            }
+            if (!__any(any)) return;
+        }
         f32x4 sc[NQ][NKB];
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi)
@@ -293,12 +341,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         // key of sc[qi][kb][e] within the tile is (wk*NKB + kb)*16 + 4*kg + e
         // cache key j of the tile is valid iff pos(j) < nck; packed key j
         // iff j < lim and its mask bit is set
-        const bool cache = i < ncache;
-        const int ic = (i + trot >= ncache) ? i + trot - ncache : i + trot;
-        const int lim = cache ? nck : tok_hi - (i - ncache) * kBlockN;
-        const bool full = cache && ic * kblk + kmul * (kBlockN - 1) < nck;  // wave-uniform
-        const int wi = 2 * (i - ncache);
-        if (!full && cache) {
+        if (KIND == kTileMasked && !packed) {
+            const int ic = tile_ic(i);
+            const int lim = nck;
             // partial cache tile: key j is valid iff its position is below lim
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi)
@@ -309,7 +354,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                         const int j = (wk * NKB + kb) * 16 + 4 * kg + e;
                         sc[qi][kb][e] = (ic * kblk + kmul * j < lim) ? sc[qi][kb][e] : -INFINITY;
                     }
-        } else if (!full) {
+        } else if (packed) {
+            const int lim = tok_hi - (i - ncache) * kBlockN;
             // packed tile: key j = jj + 4*kg (jj = (wk*NKB + kb)*16 + e) is
             // visible iff j < lim and bit j of the row's mask words is set.
             // j stays in jj's 16-key block, so its word is chosen by jj and its
@@ -317,9 +363,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             const int lim2 = lim - 4 * kg;
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi) {
-                const uint32_t w0 = mwords[lt[qi] * a.nw + wi];
-                const uint32_t w1 = (wi + 1 < a.nw) ? mwords[lt[qi] * a.nw + wi + 1] : 0u;
-                const uint32_t s0 = w0 >> (4 * kg), s1 = w1 >> (4 * kg);
+                const uint32_t s0 = mw[qi][0] >> (4 * kg), s1 = mw[qi][1] >> (4 * kg);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     const int jb = (wk * NKB + kb) * 16;  // wave-uniform
@@ -382,15 +426,22 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         // transpose loads) serves every block and is read kVPre steps ahead
         constexpr int NSTEP = NKS * NDB;
         constexpr int kVPre = 4;
-        auto vaddr = [&](int n) {
+        // four base pointers per tile (one per swizzle class db & 3); the
+        // rest of each address is a compile-time constant
+        const lds_u8 *vbase[4];
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+            vbase[d4] = reinterpret_cast<const lds_u8 *>(static_cast<uintptr_t>(sbase + voff[d4])) +
+                        wk * NKS * 32 * ROWB;
+        auto vptr = [&](int n) {
             const int ks = n / NDB, db = n % NDB;
-            return sbase + voff[db & 3] + (db >> 2) * 128 + (wk * NKS + ks) * 32 * ROWB;
+            return vbase[db & 3] + (db >> 2) * 128 + ks * 32 * ROWB;
         };
         bf16x4 vlo[kVPre], vhi[kVPre];
 #pragma unroll
         for (int n = 0; n < kVPre; ++n) {
-            vlo[n] = lds_read_tr16(vaddr(n));
-            vhi[n] = lds_read_tr16(vaddr(n) + 16 * ROWB);
+            vlo[n] = lds_read_tr16(vptr(n));
+            vhi[n] = lds_read_tr16(vptr(n) + 16 * ROWB);
         }
 #pragma unroll
         for (int n = 0; n < NSTEP; ++n) {
@@ -401,8 +452,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                 vf[4 + e] = vhi[n % kVPre][e];
             }
             if (n + kVPre < NSTEP) {
-                vlo[n % kVPre] = lds_read_tr16(vaddr(n + kVPre));
-                vhi[n % kVPre] = lds_read_tr16(vaddr(n + kVPre) + 16 * ROWB);
+                vlo[n % kVPre] = lds_read_tr16(vptr(n + kVPre));
+                vhi[n % kVPre] = lds_read_tr16(vptr(n + kVPre) + 16 * ROWB);
             }
             const int ks = n / NDB, db = n % NDB;
 #pragma unroll
@@ -451,19 +502,25 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(qf[qi][kc]));
 
-    int cslot = 0, lslot_ring = NS - 1;  // slots of the tile computed / loaded
-    for (int i = 0; i < ntile; ++i) {
+    // Two runs of the same ring loop: the full cache tiles, then the masked
+    // ones.  Separate loops keep the two compute instances' temporaries out
+    // of each other's way (one loop holding both measured register spills).
+    // Tile i sits in ring slot i % NS; tile i + NS - 1 is loaded into the
+    // slot of tile i - 1.
+    const int nact_u = nact;
+    auto tile_step = [&](int i, auto kind_c) {
         vm_wait<(NS - 2) * 2 * NLD>();
         __syncthreads();
-        issue_tile(i + NS - 1, lslot_ring);
+        const int cslot = i % NS;
+        issue_tile(i + NS - 1, (cslot + NS - 1) % NS);
         const uint32_t sbase = lds0 + cslot * STAGEB;
-        if (QPW == 2 && nact == 2)
-            compute_tile(i, sbase, std::integral_constant<int, QPW>{});
-        else if (nact >= 1)
-            compute_tile(i, sbase, std::integral_constant<int, 1>{});
-        cslot = (cslot + 1 == NS) ? 0 : cslot + 1;
-        lslot_ring = (lslot_ring + 1 == NS) ? 0 : lslot_ring + 1;
-    }
+        if (QPW == 2 && nact_u == 2)
+            compute_tile(i, sbase, std::integral_constant<int, QPW>{}, kind_c);
+        else if (nact_u >= 1)
+            compute_tile(i, sbase, std::integral_constant<int, 1>{}, kind_c);
+    };
+    for (int i = 0; i < nfull; ++i) tile_step(i, std::integral_constant<int, kTileFull>{});
+    for (int i = nfull; i < ntile; ++i) tile_step(i, std::integral_constant<int, kTileMasked>{});
     vm_wait<0>();
 
     // per-row sums over the four k-groups of the lane's column
