@@ -282,10 +282,137 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         lpart[qi] = 0.f;
     }
 
+    // The stages of one tile, for query blocks 0 .. NQ-1 (NQ from the
+    // arrays' extent).  qk_scores: S^T = K Q^T; K fragments of a head-dim
+    // step are read one step ahead and serve every block; scores stay
+    // unscaled (the scale folds into the exponent).
+    auto qk_scores = [&](uint32_t sbase, auto &sc) {
+        constexpr int NQ = sizeof(sc) / sizeof(sc[0]);
+        const uint8_t *st = stage + (sbase - lds0);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t kgrp = wk * NKB * 16 * ROWB;
+        bf16x8 ka[2][NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            ka[0][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[0] + kb * 16 * ROWB);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            if (kc + 1 < NKC)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    ka[(kc + 1) & 1][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[kc + 1] + kb * 16 * ROWB);
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[qi][kc], sc[qi][kb]);
+        }
+    };
+    // row maxima of a tile's scores in log2 units (every lane of a row's
+    // column ends with the row's value)
+    auto tile_max = [&](const auto &sc, float *tmax) {
+        constexpr int NQ = sizeof(sc) / sizeof(sc[0]);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            float t = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = fmaxf(t, sc[qi][kb][e]);
+            t = fmaxf(t, shfl_xor(t, 16));
+            t = fmaxf(t, shfl_xor(t, 32));
+            tmax[qi] = t * a.scale_log2;  // the scale is positive
+        }
+    };
+    // Lazy rescale: the reference max moves only when some row's max has
+    // grown by more than kRescale (log2 units), so O and l stay in registers
+    // untouched on most tiles.  Exact: O and l are both taken relative to
+    // the same reference, and probabilities stay below 2^kRescale.
+    auto rescale = [&](const auto &tmax) {
+        constexpr int NQ = sizeof(tmax) / sizeof(tmax[0]);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (__any(tmax[qi] > mrun[qi] + kRescale)) {
+                const float mnew = fmaxf(mrun[qi], tmax[qi]);
+                const float alpha = fast_exp2(mrun[qi] - mnew);
+                mrun[qi] = mnew;
+                lpart[qi] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[qi][db] *= alpha;
+            }
+        }
+    };
+    // probabilities against the reference max, their row sums, and P^T as
+    // the B operand of the 32-key steps: slots 0-3 hold keys 32*ks + 4*kg +
+    // (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
+    auto exps = [&](auto &sc, auto &pb) {
+        constexpr int NQ = sizeof(sc) / sizeof(sc[0]);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            const float mref = mrun[qi];
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sc[qi][kb][e] = fast_exp2(fmaf(sc[qi][kb][e], a.scale_log2, -mref));
+                    psum += sc[qi][kb][e];
+                }
+            lpart[qi] += psum;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pb[qi][ks][e] = static_cast<__bf16>(sc[qi][2 * ks][e]);
+                    pb[qi][ks][4 + e] = static_cast<__bf16>(sc[qi][2 * ks + 1][e]);
+                }
+        }
+    };
+    // O^T += V^T P^T over NKS*NDB steps (ks, db); each V^T fragment (two
+    // transpose loads) serves every block and is read kVPre steps ahead;
+    // four base pointers per tile (one per swizzle class db & 3), the rest
+    // of each address a compile-time constant
+    auto pv = [&](uint32_t sbase, const auto &pb) {
+        constexpr int NQ = sizeof(pb) / sizeof(pb[0]);
+        constexpr int NSTEP = NKS * NDB;
+        constexpr int kVPre = 4;
+        const lds_u8 *vbase[4];
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+            vbase[d4] = reinterpret_cast<const lds_u8 *>(static_cast<uintptr_t>(sbase + voff[d4])) +
+                        wk * NKS * 32 * ROWB;
+        auto vptr = [&](int n) {
+            const int ks = n / NDB, db = n % NDB;
+            return vbase[db & 3] + (db >> 2) * 128 + ks * 32 * ROWB;
+        };
+        bf16x4 vlo[kVPre], vhi[kVPre];
+#pragma unroll
+        for (int n = 0; n < kVPre; ++n) {
+            vlo[n] = lds_read_tr16(vptr(n));
+            vhi[n] = lds_read_tr16(vptr(n) + 16 * ROWB);
+        }
+#pragma unroll
+        for (int n = 0; n < NSTEP; ++n) {
+            bf16x8 vf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vf[e] = vlo[n % kVPre][e];
+                vf[4 + e] = vhi[n % kVPre][e];
+            }
+            if (n + kVPre < NSTEP) {
+                vlo[n % kVPre] = lds_read_tr16(vptr(n + kVPre));
+                vhi[n % kVPre] = lds_read_tr16(vptr(n + kVPre) + 16 * ROWB);
+            }
+            const int ks = n / NDB, db = n % NDB;
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) o[qi][db] = mfma16x16x32(vf, pb[qi][ks], o[qi][db]);
+        }
+    };
+
     // One pass over this key group's part of tile i for query blocks
-    // 0 .. NQ-1.  K fragments of a head-dim step are read one step ahead and
-    // serve every block; scores stay unscaled (the scale folds into the
-    // exponent).  KIND is the tile's kind, known before the call: a full
+    // 0 .. NQ-1.  KIND is the tile's kind, known before the call: a full
     // cache tile (no masking) or a masked one -- a partial cache tile (keys
     // past the split's end) or a packed tile (tree mask).  A separate
     // instance keeps the common full-tile path free of the masking code and
@@ -293,7 +420,6 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     auto compute_tile = [&](int i, uint32_t sbase, auto nq_c, auto kind_c) {
         constexpr int NQ = decltype(nq_c)::value;
         constexpr int KIND = decltype(kind_c)::value;
-        const uint8_t *st = stage + (sbase - lds0);
         const int wi = 2 * (i - ncache);
         const bool packed = KIND == kTileMasked && i >= ncache;  // wave-uniform
         uint32_t mw[NQ][2];  // this lane's row's mask words for the tile's two 32-key halves
@@ -316,26 +442,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             if (!__any(any)) return;
         }
         f32x4 sc[NQ][NKB];
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t kgrp = wk * NKB * 16 * ROWB;
-        bf16x8 ka[2][NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-            ka[0][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[0] + kb * 16 * ROWB);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            if (kc + 1 < NKC)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    ka[(kc + 1) & 1][kb] = *reinterpret_cast<const bf16x8 *>(st + kgrp + koff[kc + 1] + kb * 16 * ROWB);
-#pragma unroll
-            for (int qi = 0; qi < NQ; ++qi)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[qi][kc], sc[qi][kb]);
-        }
+        qk_scores(sbase, sc);
 
         // mask (partial cache tiles and packed tiles only), online softmax;
         // key of sc[qi][kb][e] within the tile is (wk*NKB + kb)*16 + 4*kg + e
@@ -377,90 +484,13 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                 }
             }
         }
+        float tmax[NQ];
+        tile_max(sc, tmax);
+        rescale(tmax);
         bf16x8 pb[NQ][NKS];
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[qi][kb][e]);
-            tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-            tmax *= a.scale_log2;  // the scale is positive
-            // Lazy rescale: the reference max moves only when some row's max
-            // has grown by more than kRescale (log2 units), so O and l stay
-            // in registers untouched on most tiles.  Exact: O and l are both
-            // taken relative to the same reference, and probabilities stay
-            // below 2^kRescale.
-            if (__any(tmax > mrun[qi] + kRescale)) {
-                const float mnew = fmaxf(mrun[qi], tmax);
-                const float alpha = fast_exp2(mrun[qi] - mnew);
-                mrun[qi] = mnew;
-                lpart[qi] *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) o[qi][db] *= alpha;
-            }
-            const float mref = mrun[qi];
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sc[qi][kb][e] = fast_exp2(fmaf(sc[qi][kb][e], a.scale_log2, -mref));
-                    psum += sc[qi][kb][e];
-                }
-            lpart[qi] += psum;
-            // P^T as the B operand of the 32-key steps: slots 0-3 hold keys
-            // 32*ks + 4*kg + (0..3), slots 4-7 keys 32*ks + 16 + 4*kg + (0..3)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pb[qi][ks][e] = static_cast<__bf16>(sc[qi][2 * ks][e]);
-                    pb[qi][ks][4 + e] = static_cast<__bf16>(sc[qi][2 * ks + 1][e]);
-                }
-        }
-
-        // O^T += V^T P^T over NKS*NDB steps (ks, db); each V^T fragment (two
-        // transpose loads) serves every block and is read kVPre steps ahead
-        constexpr int NSTEP = NKS * NDB;
-        constexpr int kVPre = 4;
-        // four base pointers per tile (one per swizzle class db & 3); the
-        // rest of each address is a compile-time constant
-        const lds_u8 *vbase[4];
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4)
-            vbase[d4] = reinterpret_cast<const lds_u8 *>(static_cast<uintptr_t>(sbase + voff[d4])) +
-                        wk * NKS * 32 * ROWB;
-        auto vptr = [&](int n) {
-            const int ks = n / NDB, db = n % NDB;
-            return vbase[db & 3] + (db >> 2) * 128 + ks * 32 * ROWB;
-        };
-        bf16x4 vlo[kVPre], vhi[kVPre];
-#pragma unroll
-        for (int n = 0; n < kVPre; ++n) {
-            vlo[n] = lds_read_tr16(vptr(n));
-            vhi[n] = lds_read_tr16(vptr(n) + 16 * ROWB);
-        }
-#pragma unroll
-        for (int n = 0; n < NSTEP; ++n) {
-            bf16x8 vf;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vf[e] = vlo[n % kVPre][e];
-                vf[4 + e] = vhi[n % kVPre][e];
-            }
-            if (n + kVPre < NSTEP) {
-                vlo[n % kVPre] = lds_read_tr16(vptr(n + kVPre));
-                vhi[n % kVPre] = lds_read_tr16(vptr(n + kVPre) + 16 * ROWB);
-            }
-            const int ks = n / NDB, db = n % NDB;
-#pragma unroll
-            for (int qi = 0; qi < NQ; ++qi) o[qi][db] = mfma16x16x32(vf, pb[qi][ks], o[qi][db]);
-        }
+        exps(sc, pb);
+        pv(sbase, pb);
     };
-
     // Ring of NS LDS stages.  Tiles 0..NS-2 are issued up front.
     // At the top of tile i this wavefront's loads of tile i have landed once
     // at most (NS-2)*2*NLD of its loads remain outstanding; the barrier
@@ -508,16 +538,18 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
     // Tile i sits in ring slot i % NS; tile i + NS - 1 is loaded into the
     // slot of tile i - 1.
     const int nact_u = nact;
+    // calls f(integral_constant<NQ>) with NQ = the wavefront's valid blocks (nothing for none)
+    auto with_nq = [&](auto f) {
+        if (QPW == 2 && nact_u == 2) f(std::integral_constant<int, QPW>{});
+        else if (nact_u >= 1) f(std::integral_constant<int, 1>{});
+    };
     auto tile_step = [&](int i, auto kind_c) {
         vm_wait<(NS - 2) * 2 * NLD>();
         __syncthreads();
         const int cslot = i % NS;
         issue_tile(i + NS - 1, (cslot + NS - 1) % NS);
         const uint32_t sbase = lds0 + cslot * STAGEB;
-        if (QPW == 2 && nact_u == 2)
-            compute_tile(i, sbase, std::integral_constant<int, QPW>{}, kind_c);
-        else if (nact_u >= 1)
-            compute_tile(i, sbase, std::integral_constant<int, 1>{}, kind_c);
+        with_nq([&](auto nq_c) { compute_tile(i, sbase, nq_c, kind_c); });
     };
     for (int i = 0; i < nfull; ++i) tile_step(i, std::integral_constant<int, kTileFull>{});
     for (int i = nfull; i < ntile; ++i) tile_step(i, std::integral_constant<int, kTileMasked>{});
