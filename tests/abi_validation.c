@@ -29,7 +29,7 @@ int main(void) {
     int32_t *fi = (int32_t *)f;
     uint32_t *fu = (uint32_t *)f;
 
-    for (int s = 0; s >= -5; --s) {
+    for (int s = 0; s >= RD_E_SCRATCH; --s) {
         const char *msg = rd_status_string(s);
         if (!msg || strncmp(msg, "RD_", 3) != 0) {
             fprintf(stderr, "status string %d: %s\n", s, msg ? msg : "(null)");
@@ -82,6 +82,11 @@ int main(void) {
     EXPECT(rd_lm_head_argmax(1, f, fi, f, 0, 8, 128, 50, f, fi, f, 0, NULL), RD_OK);
     EXPECT(rd_lm_head_argmax(1, f, fi, f, 2, 8, 0, 50, f, fi, f, 1 << 20, NULL), RD_E_ARG);
     EXPECT(rd_lm_head_workspace_size(1, -1, 8, 128, 50), 0);
+    EXPECT(rd_lm_head_argmax_noalloc(1, f, fi, f, 2, 8, 100, 50, f, fi, NULL), RD_E_UNSUPPORTED);
+    EXPECT(rd_lm_head_argmax_noalloc(1, f, fi, f, 0, 8, 128, 50, f, fi, NULL), RD_OK);
+    EXPECT(rd_lm_head_argmax_noalloc(1, NULL, fi, f, 2, 8, 128, 50, f, fi, NULL), RD_E_ARG);
+    EXPECT(rd_lm_head_workspace_size(1, 2, 40000, 4096, 32000) > RD_NOALLOC_SCRATCH_BYTES, 1);
+    EXPECT(rd_lm_head_argmax_noalloc(1, f, fi, f, 2, 40000, 4096, 32000, f, fi, NULL), RD_E_SCRATCH);
 
     /* unpack / accept */
     EXPECT(rd_unpack_accept(NULL, NULL, NULL, NULL, NULL, 1, 8, 2, 4, 0, NULL, NULL, NULL, NULL, NULL), RD_OK);
