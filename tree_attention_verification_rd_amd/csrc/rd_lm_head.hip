@@ -78,33 +78,78 @@ __device__ __forceinline__ int block_scan(int v, int *scratch, int &tot) {
     return v + before;
 }
 
-// Valid rows (p < packed_len[b]) are numbered in (b, p) order -- the compact
-// rows.  Pass 1 counts them; pass 2 records, for compact rows r0 .. r0+n-1,
-// the packed row b*P + p each one stands for.
+// Block-wide inclusive prefix maximum of one value per thread (NT threads).
 template <int NT>
-__device__ int count_rows(const int32_t *plen, int B, int P, int *scratch) {
+__device__ __forceinline__ int block_scan_max(int v, int *scratch) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, kWave);
+        if (lane >= off) v = max(v, t);
+    }
+    if (lane == 63) scratch[wave] = v;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) v = (w < wave) ? max(v, scratch[w]) : v;
+    __syncthreads();
+    return v;
+}
+
+// Valid rows (p < packed_len[b]) are numbered in (b, p) order -- the compact
+// rows.  count_rows returns their number; with B <= NT thread b also keeps
+// its request's first compact row and row count (st, cnt), so that
+// map_rows need not read the lengths again.
+template <int NT>
+__device__ int count_rows(const int32_t *plen, int B, int P, int *scratch, int &st, int &cnt) {
     int carry = 0;
+    st = 0;
+    cnt = 0;
     for (int b0 = 0; b0 < B; b0 += NT) {
         const int b = b0 + static_cast<int>(threadIdx.x);
         const int n = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
         int tot;
-        block_scan<NT>(n, scratch, tot);
+        const int incl = block_scan<NT>(n, scratch, tot);
+        if (b0 == 0) {
+            st = incl - n;
+            cnt = n;
+        }
         carry += tot;
     }
     return carry;
 }
-template <int NT>
-__device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int32_t *rmap, int *scratch) {
-    int carry = 0;
-    for (int b0 = 0; b0 < B; b0 += NT) {
-        const int b = b0 + static_cast<int>(threadIdx.x);
-        const int cnt = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
-        int tot;
-        const int start = carry + block_scan<NT>(cnt, scratch, tot) - cnt;
-        const int lo = max(start, r0), hi = min(start + cnt, r0 + n);
-        for (int m = lo; m < hi; ++m) rmap[m - r0] = b * P + (m - start);
-        carry += tot;
+// rmap[t] = packed row b*P + p of compact row r0 + t, t < n <= BR.  Each
+// request whose rows meet the range marks the tile row where they begin;
+// a prefix maximum over the tile rows then gives every row its request.
+template <int NT, int BR>
+__device__ void map_rows(const int32_t *plen, int B, int P, int r0, int n, int st, int cnt, int32_t *rmap,
+                         int32_t *head, int32_t *hstart, int *scratch) {
+    const int tid = static_cast<int>(threadIdx.x);
+    for (int i = tid; i < BR; i += NT) head[i] = -1;
+    __syncthreads();
+    auto mark = [&](int b, int s0, int c) {
+        if (c > 0 && s0 < r0 + n && s0 + c > r0) {
+            const int pos = max(s0, r0) - r0;  // distinct for distinct non-empty requests
+            head[pos] = b;
+            hstart[pos] = s0;
+        }
+    };
+    if (B <= NT) {
+        if (tid < B) mark(tid, st, cnt);
+    } else {
+        int carry = 0;
+        for (int b0 = 0; b0 < B; b0 += NT) {
+            const int b = b0 + tid;
+            const int c = (b < B) ? (plen ? min(max(plen[b], 0), P) : P) : 0;
+            int tot;
+            const int s0 = carry + block_scan<NT>(c, scratch, tot) - c;
+            if (b < B) mark(b, s0, c);
+            carry += tot;
+        }
     }
+    __syncthreads();
+    // tile row 0 always holds a mark (the request containing row r0)
+    const int at = block_scan_max<NT>((tid < BR && tid < n && head[tid] >= 0) ? tid : -1, scratch);
+    if (tid < n && tid < BR) rmap[tid] = head[at] * P + (r0 + tid - hstart[at]);
 }
 
 // SPEC: eight wavefronts, two per SIMD -- wavefronts 0-3 only multiply,
@@ -139,11 +184,13 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
     static_assert(BV % (NLD * RPL) == 0 && BR % (NLD * RPL) == 0, "each wavefront loads whole groups of both operands");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NSW * kWStage + NSX * kXStage];
     __shared__ int32_t rmap[BR];  // packed row (b*P + p) of each compact row of the tile
+    __shared__ int32_t rhead[BR], rhstart[BR];
     __shared__ int scan_tmp[NT / 64];
 
     // wave-uniform values are read into scalar registers explicitly so the
     // buffer resources built from them stay scalar (no per-lane loops)
-    const int R = __builtin_amdgcn_readfirstlane(count_rows<NT>(a.plen, a.B, a.P, scan_tmp));
+    int my_st, my_cnt;
+    const int R = __builtin_amdgcn_readfirstlane(count_rows<NT>(a.plen, a.B, a.P, scan_tmp, my_st, my_cnt));
     const int nrt = (R + BR - 1) / BR;       // row tiles that hold valid rows
     const int ntiles = nrt * a.nvt;
     const int tid = threadIdx.x;
@@ -208,20 +255,11 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
         const int vt = within / gsz;
         const int r0 = rt * BR;
         const int v0 = vt * BV;
-        map_rows<NT>(a.plen, a.B, a.P, r0, min(BR, R - r0), rmap, scan_tmp);
-        __syncthreads();
-
         const int wrows = max(0, min(a.V - v0, BV));
         const i32x4_t wres = make_srsrc(a.weight + static_cast<size_t>(min(v0, a.V)) * K,
                                         static_cast<uint32_t>(wrows) * rowb);
         // weight rows past V fall outside wres; hidden rows past R get kOOB
         const uint32_t wbase = static_cast<uint32_t>(RPL * lw + lrow) * rowb + 16 * lchunk;
-        uint32_t xbase[NLX];
-#pragma unroll
-        for (int i = 0; i < NLX; ++i) {
-            const int m = r0 + RPL * (NLD * i + lw) + lrow;
-            xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
-        }
         // The weight rows of k-step kt (k-step (kt + krot) mod nk) go to
         // weight-ring slot kt % NSW, its hidden rows to hidden-ring slot
         // kt % NSX.  The weight stream comes from HBM and is issued NSW-1
@@ -238,6 +276,21 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
             for (int i = 0; i < NLW; ++i)
                 lds_dma16(sbase + i * NLD * 1024, wres, kin ? wbase + i * NLD * RPL * rowb + kadd : kOOB);
         };
+        // The ring's first weight stages depend on the tile alone: they go
+        // out before the hidden rows are numbered, so that work overlaps
+        // their latency (the issue order of the ring is unchanged).
+        if (issues) {
+#pragma unroll
+            for (int st = 0; st <= NSW - NSX; ++st) issue_w(st, st);
+        }
+        map_rows<NT, BR>(a.plen, a.B, a.P, r0, min(BR, R - r0), my_st, my_cnt, rmap, rhead, rhstart, scan_tmp);
+        __syncthreads();
+        uint32_t xbase[NLX];
+#pragma unroll
+        for (int i = 0; i < NLX; ++i) {
+            const int m = r0 + RPL * (NLD * i + lw) + lrow;
+            xbase[i] = (m < R) ? static_cast<uint32_t>(rmap[m - r0]) * rowb + 16 * lchunk : kOOB;
+        }
         auto issue_x = [&](int kt, int slot) {
             const int kr = kstep_of(kt);
             const bool kin = kr >= 0 && kr * BK + 8 * lchunk < K;
@@ -293,10 +346,8 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
 
         if (issues) {
 #pragma unroll
-            for (int s = 0; s < NSW - NSX; ++s) issue_w(s, s);
-#pragma unroll
             for (int j = 0; j < NSX - 1; ++j) {
-                issue_w(j + NSW - NSX, j + NSW - NSX);
+                if (j > 0) issue_w(j + NSW - NSX, j + NSW - NSX);
                 issue_x(j, j);
             }
         }
