@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="dedup_p0.1")
     ap.add_argument("--variant", choices=["full", "argmax-only"], default="full")
+    ap.add_argument("--unpack", choices=["auto", "separate", "fused"], default="auto",
+                    help="full variant: gather the logits in rd_unpack_accept (separate) or in the projection "
+                         "(rd_lm_head_argmax_unpack); auto chooses by size as verify_step does")
     ap.add_argument("--rotate-mb", type=float, default=1024.0,
                     help="rotate input sets until they exceed this many MB (defeats cache residency)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -55,7 +58,8 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tree_attention_verification_rd_amd", "csrc")
-CALL_SOURCES = {"lm_head": "rd_lm_head.hip", "attention": "rd_attention.hip", "unpack": "rd_unpack_accept.hip"}
+CALL_SOURCES = {"lm_head": ("rd_lm_head.hip",), "lm_head_unpack": ("rd_lm_head.hip", "rd_unpack_accept.hip"),
+                "attention": ("rd_attention.hip",), "unpack": ("rd_unpack_accept.hip",)}
 
 
 def counted_traffic(workload: str, call: str):
@@ -73,7 +77,7 @@ def counted_traffic(workload: str, call: str):
             k, v = ln.split("=", 1)
             rec[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in (CALL_SOURCES[call], "rd_common.h", "rd_internal.h"):
+    for f in (*CALL_SOURCES[call], "rd_common.h", "rd_internal.h"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     if rec.get(f"{call}.sources_sha256") != h.hexdigest()[:16] or f"{call}.traffic_bytes" not in rec:
         return None
@@ -84,11 +88,13 @@ def traffic_source(workload: str) -> str:
     return f"profiles/{workload}_hbm_traffic.txt (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
 
 
-def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool, depth=None):
+def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits: bool, depth=None, fused=False):
     """Algorithmic traffic and work of each call (valid packed rows only; caches read once).
 
     Attention flops count 4*D per (query head, visible key): every cached key
-    plus the token's ancestors and itself (depth + 1 packed keys)."""
+    plus the token's ancestors and itself (depth + 1 packed keys).  With the
+    gather folded into the projection (fused) the projection writes every
+    candidate's row once and the unpack call moves no rows."""
     R = int(plen.sum())
     e = 2 if cfg.dtype == "bf16" else 4
     D, Hq, Hkv, K, V = cfg.D, cfg.Hq, cfg.Hkv, cfg.hidden, cfg.V
@@ -99,10 +105,10 @@ def step_bytes_and_flops(cfg, plen: np.ndarray, kv_len: np.ndarray, want_logits:
         for b in range(len(plen)):
             tree_keys += int((depth[b, :plen[b]] + 1).sum())
     attn_flops = 4 * D * Hq * (int((plen.astype(np.int64) * kv_len).sum()) + tree_keys)
-    lm_bytes = V * K * e + R * K * e + (R * V * e if want_logits else 0)
-    lm_flops = 2 * R * V * K
     cand = cfg.B * cfg.W * cfg.L
-    unpack_bytes = (R * V * e + cand * V * e) if want_logits else 0
+    lm_bytes = V * K * e + R * K * e + ((cand if fused else R) * V * e if want_logits else 0)
+    lm_flops = 2 * R * V * K
+    unpack_bytes = (R * V * e + cand * V * e) if want_logits and not fused else 0
     return {"attention": (attn_bytes, attn_flops), "lm_head": (lm_bytes, lm_flops), "unpack": (unpack_bytes, 0)}
 
 
@@ -247,6 +253,8 @@ def main():
     esz = 2 if cfg.dtype == "bf16" else 4
     seed = base_seed(cfg)
     full = args.variant == "full"
+    fused = full and (args.unpack == "fused" or
+                      (args.unpack == "auto" and rd.fuse_unpack_pays(cfg.B, cfg.W, cfg.L, cfg.V, esz)))
 
     beams = torch.from_numpy(draw_beams(cfg, seed)).to(dev)
     kv_len_np = kv_lengths(cfg)
@@ -269,11 +277,17 @@ def main():
         rd.rd_tree_attention(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], kv_len, bufs.mask,
                              pk["length"], out=bufs.attn, workspace=bufs.attn_ws)
         rec(3)
-        rd.rd_lm_head_argmax(s["hidden"], pk["length"], s["weight"], want_logits=full, logits=bufs.logits,
-                             argmax=bufs.argmax, workspace=bufs.lm_ws)
-        rec(4)
-        rd.rd_unpack_accept(beams, pk["unpacker"], bufs.argmax, bufs.logits if full else None,
-                            unpacked=bufs.unpacked, **bufs.accept)
+        if fused:
+            rd.rd_lm_head_argmax_unpack(s["hidden"], pk["length"], s["weight"], pk["unpacker"],
+                                        unpacked=bufs.unpacked, argmax=bufs.argmax, workspace=bufs.lm_ws)
+            rec(4)
+            rd.rd_unpack_accept(beams, pk["unpacker"], bufs.argmax, None, **bufs.accept)
+        else:
+            rd.rd_lm_head_argmax(s["hidden"], pk["length"], s["weight"], want_logits=full, logits=bufs.logits,
+                                 argmax=bufs.argmax, workspace=bufs.lm_ws)
+            rec(4)
+            rd.rd_unpack_accept(beams, pk["unpacker"], bufs.argmax, bufs.logits if full else None,
+                                unpacked=bufs.unpacked, **bufs.accept)
         rec(5)
 
     if args.copy_calibration_mb > 0:
@@ -423,6 +437,16 @@ def main():
             rd.rd_unpack_accept(beams, r_pk["unpacker"], bufs.argmax, bufs.logits if full else None,
                                 unpacked=bufs.unpacked, beam_width=r_bw, beam_len=r_bl, **r_acc)
 
+        # With the gather folded into the projection the step leaves no packed
+        # logits: one plain projection call provides them to the legs below
+        # (the separate gather, the ragged gather, stochastic verification).
+        gather_us = None
+        if fused:
+            rd.rd_lm_head_argmax(sets[0]["hidden"], pk["length"], sets[0]["weight"], logits=bufs.logits,
+                                 argmax=bufs.argmax, workspace=bufs.lm_ws)
+            gather_us = queued_call_us(lambda i: rd.rd_unpack_accept(
+                beams, pk["unpacker"], bufs.argmax, bufs.logits, unpacked=bufs.unpacked, **bufs.accept), lambda: None)
+
         # Stochastic step 4 on the step's own logits (full variant), with a
         # seeded draft distribution and uniforms.
         stoch_us = None
@@ -452,6 +476,7 @@ def main():
             lambda: None)
         commit_bytes = 2 * (2 * B * cfg.Hkv * cfg.L * cfg.D + B * cfg.hidden) * esz   # read + write
         extras = {
+            "separate_gather_us": None if gather_us is None else round(gather_us, 2),
             "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
                            "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
             "stochastic": {"call": "rd_stochastic_accept",
@@ -464,13 +489,15 @@ def main():
         }
 
     plen = pk["length"].cpu().numpy()
-    work = step_bytes_and_flops(cfg, plen, kv_len_np, full, pk["depth"].cpu().numpy())
+    work = step_bytes_and_flops(cfg, plen, kv_len_np, full, pk["depth"].cpu().numpy(), fused)
+    sep_work = step_bytes_and_flops(cfg, plen, kv_len_np, full, pk["depth"].cpu().numpy(), False)
+    lm_call = "rd_lm_head_argmax_unpack" if fused else "rd_lm_head_argmax"
     cand = B * cfg.W * cfg.L
 
     def roof(call, bound):
         nbytes, flops = work[call]
         t = per_call_us[call] * 1e-6
-        traffic = counted_traffic(cfg.name, call) if full else None
+        traffic = counted_traffic(cfg.name, "lm_head_unpack" if (fused and call == "lm_head") else call) if full else None
         if bound == "hbm":
             ach = nbytes / t / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -504,8 +531,9 @@ def main():
         "data": "synthetic (seeded beams from the workload's share rule; N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": cfg.name, "B": B, "W": cfg.W, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D,
                    "S": cfg.S, "V": cfg.V, "hidden": cfg.hidden, "variant": args.variant,
+                   "logits_gather": ("folded into the projection" if fused else "rd_unpack_accept") if full else None,
                    "packed_tokens": int(plen.sum()), "candidates": cand, "input_sets_rotated": n_sets},
-        "roofline": {"kernel": f"rd_{'lm_head_argmax' if dominant == 'lm_head' else 'tree_attention'}",
+        "roofline": {"kernel": lm_call if dominant == "lm_head" else "rd_tree_attention",
                      **roof(dominant, bound_of(dominant))},
         "attention_hbm": {"kernel": "rd_tree_attention", **roof("attention", "hbm"),
                           "algorithmic_flops": int(work["attention"][1]),
@@ -513,13 +541,17 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "gpu_ms_per_step": round(ms_gpu, 4),
     }
-    if full:
-        nb = work["unpack"][0]
-        ach = nb / (per_call_us["unpack_accept"] * 1e-6) / 1e9
+    # The gather's roofline: the step's rd_unpack_accept, or, when the step
+    # folds the gather into the projection, the separate call timed beside it
+    # (--legs all).
+    gather_t = per_call_us["unpack_accept"] if not fused else extras.get("separate_gather_us")
+    if full and gather_t:
+        nb = sep_work["unpack"][0]
+        ach = nb / (gather_t * 1e-6) / 1e9
         line["gather_hbm"] = {"kernel": "rd_unpack_accept", "bound": "hbm", "achieved": round(ach, 1),
                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                               "traffic": counted_traffic(cfg.name, "unpack"), "algorithmic_bytes": int(nb),
-                              "avg_us": round(per_call_us["unpack_accept"], 2)}
+                              "avg_us": round(gather_t, 2), "in_step": not fused}
     if "attention_paged" in extras:
         ap_ = extras["attention_paged"]
         ach = work["attention"][0] / (ap_["avg_us"] * 1e-6) / 1e9

@@ -286,6 +286,33 @@ int rd_lm_head_argmax_noalloc(int dtype, const void *hidden, const int32_t *pack
                               void *logits, int32_t *argmax, rd_stream_t stream);
 
 /*
+ * Steps 3 and 3b together: rd_lm_head_argmax with the unpack gather of the
+ * logits ([TRT] PyTorch `unpack`: unpacked[b,w,l,:] = logits[b,
+ * unpacker[b,w,l], :]) folded into it.  Each computed logits row is stored
+ * once, straight into the output row of the first candidate it stands for
+ * (lowest beam w); the node's other candidates are copied from that row
+ * afterwards, and padding candidates (unpacker -1) get zeros.  The packed
+ * [B,W*L,V] logits are never written and read back, so with little prefix
+ * sharing the gather costs almost nothing.  unpacked and argmax equal, bit
+ * for bit, rd_lm_head_argmax (P_max = W*L) followed by rd_unpack_accept's
+ * gather; the accept then runs as rd_unpack_accept with packed = NULL.
+ *
+ *   hidden, packed_len, weight, argmax: as rd_lm_head_argmax, P_max = W*L
+ *   unpacker (dev) [B,W,L]: from rd_pack_beams* (values in [-1, W*L))
+ *   unpacked (dev) [B,W,L,V] in dtype, written in full
+ *   ws      (dev) workspace of ws_bytes >= rd_lm_head_argmax_unpack_workspace_size()
+ * Launches: the first-candidate table (one workgroup per request), the
+ * projection, the argmax reduction and the duplicate-row copy, in order on
+ * stream.  Limits: those of rd_lm_head_argmax, W <= RD_MAX_BEAMS,
+ * L <= RD_MAX_BEAM_LEN.  B, W or L = 0 is a no-op.
+ */
+size_t rd_lm_head_argmax_unpack_workspace_size(int dtype, int B, int W, int L, int K, int V);
+int rd_lm_head_argmax_unpack(int dtype, const void *hidden, const int32_t *packed_len,
+                             const void *weight, const int32_t *unpacker, int B, int W, int L,
+                             int K, int V, void *unpacked, int32_t *argmax, void *ws,
+                             size_t ws_bytes, rd_stream_t stream);
+
+/*
  * Steps 3b and 4 -- unpack and greedy accept.
  * Unpack ([TRT] PyTorch `unpack` / TensorRT-LLM `_unpack_beams`):
  *   unpacked[b,w,l,:] = packed[b, unpacker[b,w,l], :] with rows of row_len

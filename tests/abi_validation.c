@@ -82,6 +82,14 @@ int main(void) {
     EXPECT(rd_lm_head_argmax(1, f, fi, f, 0, 8, 128, 50, f, fi, f, 0, NULL), RD_OK);
     EXPECT(rd_lm_head_argmax(1, f, fi, f, 2, 8, 0, 50, f, fi, f, 1 << 20, NULL), RD_E_ARG);
     EXPECT(rd_lm_head_workspace_size(1, -1, 8, 128, 50), 0);
+    EXPECT(rd_lm_head_argmax_unpack(1, NULL, NULL, NULL, NULL, 0, 4, 3, 128, 50, NULL, NULL, NULL, 0, NULL), RD_OK);
+    EXPECT(rd_lm_head_argmax_unpack(1, f, fi, f, fi, 2, 65, 3, 128, 50, f, fi, f, 1 << 20, NULL), RD_E_UNSUPPORTED);
+    EXPECT(rd_lm_head_argmax_unpack(1, f, fi, f, NULL, 2, 4, 3, 128, 50, f, fi, f, 1 << 20, NULL), RD_E_ARG);
+    EXPECT(rd_lm_head_argmax_unpack(1, f, fi, f, fi, 2, 4, -3, 128, 50, f, fi, f, 1 << 20, NULL), RD_E_ARG);
+    EXPECT(rd_lm_head_argmax_unpack(1, f, fi, f, fi, 2, 4, 3, 128, 50, f, fi, f, 16, NULL), RD_E_WORKSPACE);
+    EXPECT(rd_lm_head_argmax_unpack_workspace_size(1, 2, 4, 3, 128, 50) >
+               rd_lm_head_workspace_size(1, 2, 12, 128, 50), 1);
+    EXPECT(rd_lm_head_argmax_unpack_workspace_size(1, 2, 65, 3, 128, 50), 0);
     EXPECT(rd_lm_head_argmax_noalloc(1, f, fi, f, 2, 8, 100, 50, f, fi, NULL), RD_E_UNSUPPORTED);
     EXPECT(rd_lm_head_argmax_noalloc(1, f, fi, f, 0, 8, 128, 50, f, fi, NULL), RD_OK);
     EXPECT(rd_lm_head_argmax_noalloc(1, NULL, fi, f, 2, 8, 128, 50, f, fi, NULL), RD_E_ARG);

@@ -334,18 +334,22 @@ def test_verify_step_full_size(name):
     check_attention(prob, to_np(res["attn"]))
 
 
-def test_step_is_deterministic():
-    """Two runs give bit-identical outputs (logit rows past packed_len are unspecified and skipped)."""
+@pytest.mark.parametrize("fuse", [False, True])
+def test_step_is_deterministic(fuse):
+    """Two runs give bit-identical outputs (logit rows past packed_len are unspecified and skipped),
+    with the logits gathered by rd_unpack_accept or in the projection."""
     cfg = get_config("gqa").with_(B=4)
     prob = Problem(cfg, 99, checked=[0])
     outs = []
     for _ in range(2):
         r = rd.verify_step(prob.beams_t, prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache,
-                           prob.kv_len_t, prob.hidden, prob.weight)
+                           prob.kv_len_t, prob.hidden, prob.weight, fuse_unpack=fuse)
         torch.cuda.synchronize()
         o = {k: v.clone() for k, v in r.items() if isinstance(v, torch.Tensor)}
         n = prob.pack["length"]
-        o["logits"] = torch.cat([o["logits"][b, :n[b]].reshape(-1) for b in range(cfg.B)])
+        assert (o.get("logits") is None) == fuse
+        if not fuse:
+            o["logits"] = torch.cat([o["logits"][b, :n[b]].reshape(-1) for b in range(cfg.B)])
         outs.append(o)
     for k in outs[0]:
         a, b = outs[0][k], outs[1][k]

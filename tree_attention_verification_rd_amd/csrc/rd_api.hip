@@ -205,6 +205,48 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, 
                                          ws, as_stream(stream)));
 }
 
+// the unpacked projection's workspace: the projection's, then one output row per packed row
+static size_t unpack_ws_bytes(const rd::LmPlan &plan, int B, int W, int L) {
+    return plan.ws_bytes + ((static_cast<size_t>(B) * W * L * sizeof(int32_t) + 255) & ~static_cast<size_t>(255));
+}
+
+static int lm_unpack_check(int dtype, int B, int W, int L, int K, int V) {
+    if (!beam_shape_ok(B, W, L)) return RD_E_ARG;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!beam_shape_supported(W, L)) return RD_E_UNSUPPORTED;
+    return lm_check(dtype, B, W * L, K, V);
+}
+
+size_t rd_lm_head_argmax_unpack_workspace_size(int dtype, int B, int W, int L, int K, int V) {
+    if (lm_unpack_check(dtype, B, W, L, K, V) != RD_OK || B == 0 || W == 0 || L == 0) return 0;
+    return unpack_ws_bytes(rd::plan_lm_head(dtype, B, W * L, K, V), B, W, L);
+}
+
+int rd_lm_head_argmax_unpack(int dtype, const void *hidden, const int32_t *packed_len, const void *weight,
+                             const int32_t *unpacker, int B, int W, int L, int K, int V, void *unpacked,
+                             int32_t *argmax, void *ws, size_t ws_bytes, rd_stream_t stream) {
+    const int chk = lm_unpack_check(dtype, B, W, L, K, V);
+    if (chk != RD_OK) return chk;
+    if (B == 0 || W == 0 || L == 0) return RD_OK;
+    if (!hidden || !weight || !unpacker || !unpacked || !argmax) return RD_E_ARG;
+    const int P = W * L;
+    const rd::LmPlan plan = rd::plan_lm_head(dtype, B, P, K, V);
+    if (!ws || ws_bytes < unpack_ws_bytes(plan, B, W, L)) return RD_E_WORKSPACE;
+    const int dbg = debug_check(stream, {{packed_len, packed_len ? B : 0, 0, P + 1},
+                                         {unpacker, B * P, -1, P}});
+    if (dbg != RD_OK) return dbg;
+    int32_t *node_row = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + plan.ws_bytes);
+    const hipStream_t s = as_stream(stream);
+    hipError_t err = rd::launch_node_rows(unpacker, B, W, L, node_row, s);
+    if (err == hipSuccess)
+        err = rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P, K, V, unpacked, argmax, ws, s,
+                                 node_row);
+    if (err == hipSuccess)
+        err = rd::launch_unpack_dups(unpacked, unpacker, node_row,
+                                     static_cast<int64_t>(V) * (dtype == RD_BF16 ? 2 : 4), B, W, L, s);
+    return hip_status(err);
+}
+
 int rd_lm_head_argmax_noalloc(int dtype, const void *hidden, const int32_t *packed_len, const void *weight, int B,
                               int P_max, int K, int V, void *logits, int32_t *argmax, rd_stream_t stream) {
     const int chk = lm_check(dtype, B, P_max, K, V);

@@ -57,7 +57,7 @@ struct LmPlan {
 LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V);
 hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, const int32_t *plen,
                           const void *weight, int B, int P_max, int K, int V, void *logits,
-                          int32_t *argmax, void *ws, hipStream_t stream);
+                          int32_t *argmax, void *ws, hipStream_t stream, const int32_t *node_row = nullptr);
 // device address of the current device's fixed projection scratch (RD_NOALLOC_SCRATCH_BYTES)
 hipError_t noalloc_scratch(void **out);
 
@@ -67,6 +67,14 @@ hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_
                                 int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
                                 int32_t *accepted, hipStream_t stream, const int32_t *bwid = nullptr,
                                 const int32_t *blen = nullptr);
+
+// unpack folded into the projection: node_row[b*P + p] = output row
+// (b*W + w)*L + l of packed row p's first candidate (lowest w), -1 for a row
+// no candidate stands for; then every other candidate row is copied from its
+// node's first one (padding candidates, unpacker -1, get zeros)
+hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, hipStream_t stream);
+hipError_t launch_unpack_dups(void *unpacked, const int32_t *unpacker, const int32_t *node_row, int64_t row_bytes,
+                              int B, int W, int L, hipStream_t stream);
 
 // commit of the accepted path (esize = bytes per element)
 hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,

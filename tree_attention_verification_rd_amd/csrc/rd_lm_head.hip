@@ -45,6 +45,11 @@ struct LmArgs {
     const int32_t *plen;  // packed lengths [B] (clamped to [0, P]); null: all P rows valid
     int B, P, K, V;
     uint16_t *logits;
+    // null: logits row b*P + p is packed row b*P + p; otherwise logits is the
+    // unpacked [B, W, L, V] output and the row goes to output row
+    // node_row[b*P + p] (the node's first candidate; the unpack gather
+    // folded into the epilogue)
+    const int32_t *node_row;
     float *pval;
     int32_t *pidx;
     int nvt, nrt;
@@ -440,6 +445,7 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
                 int bi = 0x7fffffff;
                 if (active) {
                     const int pr = mvalid ? rmap[m - r0] : 0;
+                    const int64_t orow = (a.node_row && mvalid) ? a.node_row[pr] : pr;
 #pragma unroll
                     for (int vb = 0; vb < NVB; ++vb) {
                         const int v = v0 + gv * WV + vb * 16 + 4 * kg;
@@ -452,7 +458,7 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
                             bi = take ? v + e : bi;
                         }
                         if (a.logits && mvalid) {
-                            uint16_t *dst = a.logits + static_cast<size_t>(pr) * a.V + v;
+                            uint16_t *dst = a.logits + static_cast<size_t>(orow) * a.V + v;
                             if (v + 3 < a.V && (a.V % 4 == 0)) {
                                 u16x4 w = {f32_to_bf16_bits(acc[vb][rb][0]), f32_to_bf16_bits(acc[vb][rb][1]),
                                            f32_to_bf16_bits(acc[vb][rb][2]), f32_to_bf16_bits(acc[vb][rb][3])};
@@ -512,8 +518,9 @@ __global__ __launch_bounds__(SPEC ? 512 : 64 * NWV, 1) void k_lm_head_bf16(LmArg
 __global__ __launch_bounds__(256) void k_lm_head_f32(const float *__restrict__ hidden,
                                                      const int32_t *__restrict__ plen,
                                                      const float *__restrict__ weight, int P, int K, int V,
-                                                     float *__restrict__ logits, float *__restrict__ pval,
-                                                     int32_t *__restrict__ pidx, int nvt) {
+                                                     float *__restrict__ logits,
+                                                     const int32_t *__restrict__ node_row,
+                                                     float *__restrict__ pval, int32_t *__restrict__ pidx, int nvt) {
     __shared__ float hs[1024];
     __shared__ float rv[256];
     __shared__ int32_t ri[256];
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(256) void k_lm_head_f32(const float *__restrict__ h
         __syncthreads();
         for (int k = 0; k < kn; ++k) acc = fmaf(hs[k], wr[k0 + k], acc);
     }
-    if (v < V && logits) logits[pr * V + v] = acc;
+    if (v < V && logits) logits[(node_row ? static_cast<size_t>(node_row[pr]) : pr) * V + v] = acc;
     rv[threadIdx.x] = (v < V) ? acc : -INFINITY;
     ri[threadIdx.x] = (v < V) ? v : 0x7fffffff;
     __syncthreads();
@@ -663,7 +670,7 @@ LmPlan plan_lm_head(int dtype, int B, int P_max, int K, int V) {
 
 hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, const int32_t *plen,
                           const void *weight, int B, int P_max, int K, int V, void *logits, int32_t *argmax,
-                          void *ws, hipStream_t stream) {
+                          void *ws, hipStream_t stream, const int32_t *node_row) {
     char *w = static_cast<char *>(ws);
     const size_t rows = static_cast<size_t>(plan.rows_pad);
     float *pval = reinterpret_cast<float *>(w);
@@ -672,7 +679,7 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
     if (dtype == 0) {
         hipLaunchKernelGGL(k_lm_head_f32, dim3(static_cast<unsigned>(rows * plan.nvt)), dim3(256), 0, stream,
                            static_cast<const float *>(hidden), plen, static_cast<const float *>(weight), P_max, K,
-                           V, static_cast<float *>(logits), pval, pidx, plan.nvt);
+                           V, static_cast<float *>(logits), node_row, pval, pidx, plan.nvt);
     } else {
         LmArgs a;
         a.hidden = static_cast<const uint16_t *>(hidden);
@@ -683,6 +690,7 @@ hipError_t launch_lm_head(int dtype, const LmPlan &plan, const void *hidden, con
         a.K = K;
         a.V = V;
         a.logits = static_cast<uint16_t *>(logits);
+        a.node_row = node_row;
         a.pval = pval;
         a.pidx = pidx;
         a.nvt = plan.nvt;

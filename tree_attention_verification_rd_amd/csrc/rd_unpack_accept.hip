@@ -95,6 +95,86 @@ __global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ pac
     }
 }
 
+// The unpack folded into the projection (the same gather, other order).
+// Each packed row is written once, by the projection, to the output row of
+// its first candidate -- the lowest beam w with unpacker[b,w,l] = p, all of
+// a node's candidates sharing its depth l -- and the node's other candidates
+// are copied from that row afterwards.  With little prefix sharing almost
+// every row has one candidate and the copy has almost nothing to do.
+__global__ __launch_bounds__(256) void k_node_rows(const int32_t *__restrict__ unpacker, int W, int L,
+                                                   int32_t *__restrict__ node_row) {
+    __shared__ int first_w[kMaxBeams * kMaxBeamLen];
+    __shared__ int depth[kMaxBeams * kMaxBeamLen];
+    const int b = blockIdx.x;
+    const int WL = W * L;
+    for (int p = threadIdx.x; p < WL; p += 256) first_w[p] = kMaxBeams;
+    __syncthreads();
+    for (int c = threadIdx.x; c < WL; c += 256) {
+        const int p = unpacker[static_cast<size_t>(b) * WL + c];
+        if (p >= 0 && p < WL) {
+            const int w = c / L;
+            atomicMin(&first_w[p], w);
+            depth[p] = c - w * L;  // every candidate of node p has its depth
+        }
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < WL; p += 256)
+        node_row[static_cast<size_t>(b) * WL + p] =
+            first_w[p] < kMaxBeams ? b * WL + first_w[p] * L + depth[p] : -1;
+}
+
+template <typename T, int UNROLL>
+__global__ __launch_bounds__(256) void k_unpack_dups(T *__restrict__ out, const int32_t *__restrict__ unpacker,
+                                                     const int32_t *__restrict__ node_row, int64_t row_elems, int WL,
+                                                     int nchunks) {
+    const int64_t blk = blockIdx.x;
+    const int64_t row = blk / nchunks;
+    const int chunk = static_cast<int>(blk % nchunks);
+    const int64_t b = row / WL;
+    const int uslot = unpacker[row];
+    const int64_t src = uslot >= 0 ? node_row[b * WL + min(uslot, WL - 1)] : -1;
+    if (src == row) return;  // the node's first candidate: written by the projection
+    const T *s = out + src * row_elems;
+    T *d = out + row * row_elems;
+    const int64_t base = static_cast<int64_t>(chunk) * (256 * UNROLL) + threadIdx.x;
+    T v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < row_elems) v[u] = (src >= 0) ? s[i] : T{};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+        const int64_t i = base + u * 256;
+        if (i < row_elems) __builtin_nontemporal_store(v[u], d + i);
+    }
+}
+
+hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, hipStream_t stream) {
+    hipLaunchKernelGGL(k_node_rows, dim3(B), dim3(256), 0, stream, unpacker, W, L, node_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_dups(void *unpacked, const int32_t *unpacker, const int32_t *node_row, int64_t row_bytes,
+                              int B, int W, int L, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(B) * W * L;
+    constexpr int U = 4;
+    auto go = [&](auto *dst, int64_t elems) {
+        using T = std::remove_pointer_t<decltype(dst)>;
+        const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
+        hipLaunchKernelGGL((k_unpack_dups<T, U>), dim3(static_cast<unsigned>(rows * nchunks)), dim3(256), 0, stream,
+                           dst, unpacker, node_row, elems, W * L, nchunks);
+    };
+    const uintptr_t align = reinterpret_cast<uintptr_t>(unpacked);
+    if (row_bytes % 16 == 0 && align % 16 == 0)
+        go(static_cast<u32x4 *>(unpacked), row_bytes / 16);
+    else if (row_bytes % 4 == 0 && align % 4 == 0)
+        go(static_cast<uint32_t *>(unpacked), row_bytes / 4);
+    else
+        go(static_cast<uint8_t *>(unpacked), row_bytes);
+    return hipGetLastError();
+}
+
 hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_t *unpacker, int64_t row_bytes,
                                 const int32_t *beams, const int32_t *pargmax, int B, int W, int L,
                                 int32_t *match_len, int32_t *best_beam, int32_t *accept_len,
