@@ -205,9 +205,12 @@ int rd_lm_head_argmax(int dtype, const void *hidden, const int32_t *packed_len, 
                                          ws, as_stream(stream)));
 }
 
-// the unpacked projection's workspace: the projection's, then one output row per packed row
+// the unpacked projection's workspace: the projection's, then per packed row its
+// output row, per candidate one entry of the fill list, per request the list length
+static size_t ws_round(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 static size_t unpack_ws_bytes(const rd::LmPlan &plan, int B, int W, int L) {
-    return plan.ws_bytes + ((static_cast<size_t>(B) * W * L * sizeof(int32_t) + 255) & ~static_cast<size_t>(255));
+    const size_t n = static_cast<size_t>(B) * W * L;
+    return plan.ws_bytes + ws_round(n * sizeof(int32_t)) + ws_round(n * sizeof(int2)) + ws_round(B * sizeof(int32_t));
 }
 
 static int lm_unpack_check(int dtype, int B, int W, int L, int K, int V) {
@@ -235,15 +238,19 @@ int rd_lm_head_argmax_unpack(int dtype, const void *hidden, const int32_t *packe
     const int dbg = debug_check(stream, {{packed_len, packed_len ? B : 0, 0, P + 1},
                                          {unpacker, B * P, -1, P}});
     if (dbg != RD_OK) return dbg;
-    int32_t *node_row = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + plan.ws_bytes);
+    const size_t n = static_cast<size_t>(B) * P;
+    char *w = static_cast<char *>(ws) + plan.ws_bytes;
+    int32_t *node_row = reinterpret_cast<int32_t *>(w);
+    int2 *todo = reinterpret_cast<int2 *>(w + ws_round(n * sizeof(int32_t)));
+    int32_t *ntodo = reinterpret_cast<int32_t *>(w + ws_round(n * sizeof(int32_t)) + ws_round(n * sizeof(int2)));
     const hipStream_t s = as_stream(stream);
-    hipError_t err = rd::launch_node_rows(unpacker, B, W, L, node_row, s);
+    hipError_t err = rd::launch_node_rows(unpacker, B, W, L, node_row, todo, ntodo, s);
     if (err == hipSuccess)
         err = rd::launch_lm_head(dtype, plan, hidden, packed_len, weight, B, P, K, V, unpacked, argmax, ws, s,
                                  node_row);
     if (err == hipSuccess)
-        err = rd::launch_unpack_dups(unpacked, unpacker, node_row,
-                                     static_cast<int64_t>(V) * (dtype == RD_BF16 ? 2 : 4), B, W, L, s);
+        err = rd::launch_unpack_dups(unpacked, todo, ntodo, static_cast<int64_t>(V) * (dtype == RD_BF16 ? 2 : 4), B,
+                                     W, L, s);
     return hip_status(err);
 }
 

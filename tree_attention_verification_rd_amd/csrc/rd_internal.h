@@ -70,11 +70,12 @@ hipError_t launch_unpack_accept(const void *packed, void *unpacked, const int32_
 
 // unpack folded into the projection: node_row[b*P + p] = output row
 // (b*W + w)*L + l of packed row p's first candidate (lowest w), -1 for a row
-// no candidate stands for; then every other candidate row is copied from its
-// node's first one (padding candidates, unpacker -1, get zeros)
-hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, hipStream_t stream);
-hipError_t launch_unpack_dups(void *unpacked, const int32_t *unpacker, const int32_t *node_row, int64_t row_bytes,
-                              int B, int W, int L, hipStream_t stream);
+// no candidate stands for; todo[b*P + j], j < ntodo[b], lists request b's
+// other output rows as (row, source row or -1 for zeros), filled afterwards
+hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, int2 *todo,
+                            int32_t *ntodo, hipStream_t stream);
+hipError_t launch_unpack_dups(void *unpacked, const int2 *todo, const int32_t *ntodo, int64_t row_bytes, int B,
+                              int W, int L, hipStream_t stream);
 
 // commit of the accepted path (esize = bytes per element)
 hipError_t launch_commit(int esize, const int32_t *unpacker, const int32_t *best_beam, const int32_t *accept_len,

@@ -98,19 +98,25 @@ __global__ __launch_bounds__(256) void k_unpack_accept(const T *__restrict__ pac
 // The unpack folded into the projection (the same gather, other order).
 // Each packed row is written once, by the projection, to the output row of
 // its first candidate -- the lowest beam w with unpacker[b,w,l] = p, all of
-// a node's candidates sharing its depth l -- and the node's other candidates
-// are copied from that row afterwards.  With little prefix sharing almost
-// every row has one candidate and the copy has almost nothing to do.
+// a node's candidates sharing its depth l.  k_node_rows finds those rows and
+// lists, per request, the output rows still to fill afterwards: the node's
+// other candidates (copied from its first) and padding candidates (zeros).
+// With little prefix sharing the lists are short, and the copy kernel only
+// walks them.
 __global__ __launch_bounds__(256) void k_node_rows(const int32_t *__restrict__ unpacker, int W, int L,
-                                                   int32_t *__restrict__ node_row) {
+                                                   int32_t *__restrict__ node_row, int2 *__restrict__ todo,
+                                                   int32_t *__restrict__ ntodo) {
     __shared__ int first_w[kMaxBeams * kMaxBeamLen];
     __shared__ int depth[kMaxBeams * kMaxBeamLen];
+    __shared__ int count;
     const int b = blockIdx.x;
     const int WL = W * L;
+    const int32_t *u = unpacker + static_cast<size_t>(b) * WL;
     for (int p = threadIdx.x; p < WL; p += 256) first_w[p] = kMaxBeams;
+    if (threadIdx.x == 0) count = 0;
     __syncthreads();
     for (int c = threadIdx.x; c < WL; c += 256) {
-        const int p = unpacker[static_cast<size_t>(b) * WL + c];
+        const int p = u[c];
         if (p >= 0 && p < WL) {
             const int w = c / L;
             atomicMin(&first_w[p], w);
@@ -119,51 +125,77 @@ __global__ __launch_bounds__(256) void k_node_rows(const int32_t *__restrict__ u
     }
     __syncthreads();
     for (int p = threadIdx.x; p < WL; p += 256)
-        node_row[static_cast<size_t>(b) * WL + p] =
-            first_w[p] < kMaxBeams ? b * WL + first_w[p] * L + depth[p] : -1;
+        node_row[static_cast<size_t>(b) * WL + p] = first_w[p] < kMaxBeams ? b * WL + first_w[p] * L + depth[p] : -1;
+    // output rows the projection does not write: (row, source row or -1 for zeros)
+    for (int c = threadIdx.x; c < WL; c += 256) {
+        const int p = u[c];
+        const int src = (p >= 0 && p < WL) ? b * WL + first_w[p] * L + depth[p] : -1;
+        if (src != b * WL + c) todo[static_cast<size_t>(b) * WL + atomicAdd(&count, 1)] = make_int2(b * WL + c, src);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) ntodo[b] = count;
 }
 
-template <typename T, int UNROLL>
-__global__ __launch_bounds__(256) void k_unpack_dups(T *__restrict__ out, const int32_t *__restrict__ unpacker,
-                                                     const int32_t *__restrict__ node_row, int64_t row_elems, int WL,
-                                                     int nchunks) {
-    const int64_t blk = blockIdx.x;
-    const int64_t row = blk / nchunks;
-    const int chunk = static_cast<int>(blk % nchunks);
-    const int64_t b = row / WL;
-    const int uslot = unpacker[row];
-    const int64_t src = uslot >= 0 ? node_row[b * WL + min(uslot, WL - 1)] : -1;
-    if (src == row) return;  // the node's first candidate: written by the projection
-    const T *s = out + src * row_elems;
-    T *d = out + row * row_elems;
-    const int64_t base = static_cast<int64_t>(chunk) * (256 * UNROLL) + threadIdx.x;
-    T v[UNROLL];
+// Request b's list is cut into (entry, chunk of 256*UNROLL elements) items;
+// workgroup (b, s) fills items s, s + S, ..., IB at a time, each thread with
+// IB*UNROLL vector loads in flight, so a short list costs a few idle
+// workgroups and a long one spreads over many without waiting on one load
+// round trip per item.
+template <typename T, int UNROLL, int IB>
+__global__ __launch_bounds__(256) void k_unpack_dups(T *__restrict__ out, const int2 *__restrict__ todo,
+                                                     const int32_t *__restrict__ ntodo, int64_t row_elems, int WL,
+                                                     int nchunks, int S) {
+    const int b = blockIdx.x / S;
+    const int s = blockIdx.x % S;
+    const int items = ntodo[b] * nchunks;
+    for (int it0 = s; it0 < items; it0 += S * IB) {
+        T v[IB][UNROLL];
+        int2 e[IB];
+        int64_t base[IB];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-        const int64_t i = base + u * 256;
-        if (i < row_elems) v[u] = (src >= 0) ? s[i] : T{};
-    }
+        for (int q = 0; q < IB; ++q) {
+            const int it = it0 + q * S;
+            const int j = (it < items) ? it / nchunks : 0;
+            e[q] = (it < items) ? todo[static_cast<size_t>(b) * WL + j] : make_int2(-1, -1);
+            base[q] = static_cast<int64_t>(it - j * nchunks) * (256 * UNROLL) + threadIdx.x;
+        }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-        const int64_t i = base + u * 256;
-        if (i < row_elems) __builtin_nontemporal_store(v[u], d + i);
+        for (int q = 0; q < IB; ++q) {
+            const T *src = out + static_cast<int64_t>(e[q].y) * row_elems;
+#pragma unroll
+            for (int k = 0; k < UNROLL; ++k) {
+                const int64_t i = base[q] + k * 256;
+                if (e[q].x >= 0 && i < row_elems) v[q][k] = (e[q].y >= 0) ? src[i] : T{};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < IB; ++q) {
+            T *dst = out + static_cast<int64_t>(e[q].x) * row_elems;
+#pragma unroll
+            for (int k = 0; k < UNROLL; ++k) {
+                const int64_t i = base[q] + k * 256;
+                if (e[q].x >= 0 && i < row_elems) __builtin_nontemporal_store(v[q][k], dst + i);
+            }
+        }
     }
 }
 
-hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, hipStream_t stream) {
-    hipLaunchKernelGGL(k_node_rows, dim3(B), dim3(256), 0, stream, unpacker, W, L, node_row);
+hipError_t launch_node_rows(const int32_t *unpacker, int B, int W, int L, int32_t *node_row, int2 *todo,
+                            int32_t *ntodo, hipStream_t stream) {
+    hipLaunchKernelGGL(k_node_rows, dim3(B), dim3(256), 0, stream, unpacker, W, L, node_row, todo, ntodo);
     return hipGetLastError();
 }
 
-hipError_t launch_unpack_dups(void *unpacked, const int32_t *unpacker, const int32_t *node_row, int64_t row_bytes,
-                              int B, int W, int L, hipStream_t stream) {
-    const int64_t rows = static_cast<int64_t>(B) * W * L;
+hipError_t launch_unpack_dups(void *unpacked, const int2 *todo, const int32_t *ntodo, int64_t row_bytes, int B,
+                              int W, int L, hipStream_t stream) {
+    // workgroups per request: enough to spread a long list over the CUs
+    constexpr int S = 32;
     constexpr int U = 4;
     auto go = [&](auto *dst, int64_t elems) {
         using T = std::remove_pointer_t<decltype(dst)>;
         const int nchunks = static_cast<int>((elems + 256 * U - 1) / (256 * U));
-        hipLaunchKernelGGL((k_unpack_dups<T, U>), dim3(static_cast<unsigned>(rows * nchunks)), dim3(256), 0, stream,
-                           dst, unpacker, node_row, elems, W * L, nchunks);
+        hipLaunchKernelGGL((k_unpack_dups<T, U, 4>), dim3(static_cast<unsigned>(B * S)), dim3(256), 0, stream, dst,
+                           todo, ntodo, elems, W * L, nchunks, S);
     };
     const uintptr_t align = reinterpret_cast<uintptr_t>(unpacked);
     if (row_bytes % 16 == 0 && align % 16 == 0)
