@@ -74,6 +74,16 @@ __device__ __forceinline__ int64_t page_of(const AttnArgs &a, int b, int t) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Maximum over lanes i, i^16, i^32 and i^48 (the four k-groups of an MFMA
+// output column), without LDS: v_permlane32_swap (v_permlane16_swap) with
+// both operands t leaves t of lanes i and i^32 (i^16) in its two results.
+__device__ __forceinline__ float max_over_kgroups(float t) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    t = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     bf16x8 r;
     __builtin_memcpy(&r, &v, 16);
@@ -310,8 +320,8 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                 for (int kb = 0; kb < NKB; ++kb) sc[qi][kb] = mfma16x16x32(ka[kc & 1][kb], qf[qi][kc], sc[qi][kb]);
         }
     };
-    // row maxima of a tile's scores in log2 units (every lane of a row's
-    // column ends with the row's value)
+    // maxima of a tile's scores in log2 units over each lane's own keys of
+    // its row (the row maximum is the largest of its four k-groups' values)
     auto tile_max = [&](const auto &sc, float *tmax) {
         constexpr int NQ = sizeof(sc) / sizeof(sc[0]);
 #pragma unroll
@@ -321,21 +331,21 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) t = fmaxf(t, sc[qi][kb][e]);
-            t = fmaxf(t, shfl_xor(t, 16));
-            t = fmaxf(t, shfl_xor(t, 32));
             tmax[qi] = t * a.scale_log2;  // the scale is positive
         }
     };
     // Lazy rescale: the reference max moves only when some row's max has
     // grown by more than kRescale (log2 units), so O and l stay in registers
     // untouched on most tiles.  Exact: O and l are both taken relative to
-    // the same reference, and probabilities stay below 2^kRescale.
+    // the same reference, and probabilities stay below 2^kRescale.  Some
+    // row has grown that much iff some lane's own maximum has, so the
+    // cross-lane reduction runs only on the tiles that rescale.
     auto rescale = [&](const auto &tmax) {
         constexpr int NQ = sizeof(tmax) / sizeof(tmax[0]);
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
             if (__any(tmax[qi] > mrun[qi] + kRescale)) {
-                const float mnew = fmaxf(mrun[qi], tmax[qi]);
+                const float mnew = fmaxf(mrun[qi], max_over_kgroups(tmax[qi]));
                 const float alpha = fast_exp2(mrun[qi] - mnew);
                 mrun[qi] = mnew;
                 lpart[qi] *= alpha;
