@@ -15,8 +15,9 @@ oracle (per-beam attention over the same bf16-rounded inputs):
   is the same for every key of a row, so the softmax is that of the
   unshifted scores.
 
-Each runs on a few rows (4 wavefronts, two key groups), on many rows (8
-wavefronts) and at D = 64, with and without a forced split of the cache.
+Each runs on a few rows (8 wavefronts, two key groups), on many rows (8
+wavefronts), on a GQA group of 160 rows and at D = 64, with and without a
+forced split of the cache.
 """
 import sys
 
@@ -47,6 +48,7 @@ SHAPES = {
     "few_rows": get_config("llama_mha").with_(B=2, W=4, L=5, Hq=4, Hkv=4, S=300, V=512),
     "many_rows": get_config("dedup_p0.5").with_(B=2, Hq=2, Hkv=2, S=200, V=512),
     "gqa_d64": get_config("gqa").with_(B=2, W=16, L=5, Hq=8, Hkv=2, D=64, S=260, V=512),
+    "mid_rows": get_config("gqa").with_(B=2, W=8, L=5, Hq=8, Hkv=2, D=128, S=330, V=512),
 }
 
 

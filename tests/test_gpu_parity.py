@@ -180,6 +180,9 @@ SMALL_ATTN = {
     "bf16_gqa_d64": get_config("gqa").with_(B=2, W=16, L=5, Hq=8, Hkv=2, D=64, S=130, V=512),
     "bf16_big_tree": get_config("dedup_p0.5").with_(B=2, Hq=2, Hkv=2, S=70, V=512),
     "bf16_no_cache": get_config("llama_mha").with_(B=2, W=4, L=6, Hq=4, Hkv=4, S=0, V=512),
+    # GQA groups of 160 and 192 rows per (request, KV head)
+    "bf16_gqa_mid_rows": get_config("gqa").with_(B=3, W=8, L=5, Hq=8, Hkv=2, D=128, S=300, V=512),
+    "bf16_gqa_mid_rows_d64": get_config("gqa").with_(B=2, W=12, L=4, Hq=8, Hkv=2, D=64, S=190, V=512),
 }
 
 
