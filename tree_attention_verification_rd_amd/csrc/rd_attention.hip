@@ -240,7 +240,6 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
         i32x4_t rv = cache ? rv_c : rv_n;
         const int ic = tile_ic(i);
         const int kbase = cache ? c0 + ic * kblk : (i - ncache) * kBlockN;
-        const int kstep = cache ? kmul : 1;
         const int klim = (i >= ntile) ? 0 : (cache ? c1v : tok_hi);
         const uint32_t rowstride = cache ? ROWB : static_cast<uint32_t>(a.Hkv) * ROWB;
         const uint32_t kdst = lds0 + slot * STAGEB;
@@ -254,13 +253,23 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void k_tree_attn_bf16(AttnArgs a) {
                 kres = kbase;
             }
         }
+        // Lane offsets from the tile's first key: kk keys and, to the lane's
+        // chunk, lo bytes -- keys kmul apart in rows of ROWB bytes for a cache
+        // tile, consecutive keys in rows of Hkv*ROWB bytes for a packed one.
+        // Both forms are loop-invariant values (hoisted), so a tile's loads
+        // select between them and multiply nothing.
+        const int krem = klim - kbase;  // keys kbase + kk with kk < krem are in range
+        const uint32_t obase = static_cast<uint32_t>(kbase - kres) * rowstride;
 #pragma unroll
         for (int jj = 0; jj < NLD; ++jj) {
             const int j = NWAVE * jj + wave;
             const int kl = KPL * j + lkey;
-            const int key = kbase + kstep * kl;
-            const uint32_t off =
-                key < klim ? static_cast<uint32_t>(key - kres) * rowstride + ((lslot ^ (kl & 7)) << 4) : kOOB;
+            const uint32_t sw = static_cast<uint32_t>(lslot ^ (kl & 7)) << 4;
+            const int kk_c = kmul * kl;
+            const uint32_t lo_c = static_cast<uint32_t>(kk_c) * ROWB + sw;
+            const uint32_t lo_n = static_cast<uint32_t>(kl) * (static_cast<uint32_t>(a.Hkv) * ROWB) + sw;
+            const int kk = cache ? kk_c : kl;
+            const uint32_t off = kk < krem ? obase + (cache ? lo_c : lo_n) : kOOB;
             lds_dma16(kdst + j * 1024, rk, off);
             lds_dma16(kdst + TILEB + j * 1024, rv, off);
         }
