@@ -14,7 +14,12 @@
 // rows where p0 <= c_i q staying zero.  The sequence (c_i, D_i) of a node
 // depends on its p0 and q only, not on the uniforms, so it is computed for
 // every node at once:
-//   k_stoch_node  -- one workgroup per (request, slot): the max and sum of
+//   k_stoch_rows  -- bf16 logits, V a multiple of 8 and at most 32768 (the
+//                    rows the workloads have): the statistics listed next,
+//                    in persistent workgroups of 512 threads that hold a row
+//                    in registers (64 entries a thread) and load the next
+//                    slot's row while computing the current one (see there);
+//   k_stoch_node  -- otherwise, one workgroup per (request, slot): the max and sum of
 //                    the slot's logits, (c_i, D_i) for i up to its child
 //                    count nk, the pair (p_i(x), q(x)) that its i-th child
 //                    (token x) is tested with, stored with that child, and
@@ -45,6 +50,8 @@
 // All sums run in a fixed order, so results are deterministic.
 #include <math.h>
 
+#include <algorithm>
+
 #include "rd_common.h"
 #include "rd_internal.h"
 
@@ -62,7 +69,7 @@ struct StochArgs {
     const float *q;      // [B,P,V]
     const float *u_acc;  // [B,L,W]
     const float *u_bonus;
-    int W, L, V, is_bf16;
+    int B, W, L, V, is_bf16;
     int32_t *best_beam, *accept_len, *accepted, *path;
     float2 *test;    // [B,P]: (p_i(x), q(x)) of the slot's test at its parent (x its token, i its rank)
     int32_t *bonus;  // [B,P]: the slot's bonus token when all its children are rejected
@@ -76,29 +83,58 @@ __device__ __forceinline__ float load_logit(const StochArgs &a, size_t i) {
     return static_cast<const float *>(a.logits)[i];
 }
 
-// Block reductions (fixed order: lanes by xor shuffles, then wavefronts in
-// index order).  red is LDS scratch of kNW floats.
+// Sum or maximum over the 64 lanes of a wavefront, the same bits in every
+// lane, without LDS round trips: lanes i and i^32 by v_permlane32_swap, i
+// and i^16 by v_permlane16_swap (with both operands v each leaves the two
+// lanes' values in its two results), then within each row of 16 lanes DPP
+// rotations by 8, 4, 2 and 1.  Each step combines two equal partial results
+// with a commutative operation, so all lanes agree.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    v = op(v, dpp_f<0x128>(v));  // row_ror:8
+    v = op(v, dpp_f<0x124>(v));  // row_ror:4
+    v = op(v, dpp_f<0x122>(v));  // row_ror:2
+    v = op(v, dpp_f<0x121>(v));  // row_ror:1
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    return wave_reduce(v, [](float x, float y) { return x + y; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+    return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+
+// Block reductions (fixed order: the wavefront's lanes as above, then
+// wavefronts in index order).  red is LDS scratch of kNW floats.
+template <int NT = kT>
 __device__ __forceinline__ float block_sum(float v, float *red) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
+    v = wave_sum(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) t += red[w];
+    for (int w = 0; w < (NT / kWave); ++w) t += red[w];
     return t;
 }
 
+template <int NT = kT>
 __device__ __forceinline__ float block_max(float v, float *red) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, shfl_xor(v, off));
+    v = wave_max(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float t = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) t = fmaxf(t, red[w]);
+    for (int w = 0; w < (NT / kWave); ++w) t = fmaxf(t, red[w]);
     return t;
 }
 
@@ -132,19 +168,34 @@ __device__ __forceinline__ float block_softmax_stats(float m, float s, float *re
 
 // Inclusive block scan of one float per thread; returns the thread's
 // inclusive prefix and the block total.
+// Inclusive scan over the lanes of a wavefront, without LDS round trips:
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes (lanes shifted in from
+// outside the row read 0), then the last lane of row 0 (2) added to row 1
+// (3), then the last lane of row 1 to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f0(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float wave_scan_incl(float v) {
+    v += dpp_f0<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_f0<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_f0<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_f0<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_f0<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f0<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+template <int NT = kT>
 __device__ __forceinline__ float block_scan(float v, float *red, float &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
+    v = wave_scan_incl(v);
     __syncthreads();
     if (lane == 63) red[wave] = v;
     __syncthreads();
     float before = 0.f, t = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < (NT / kWave); ++w) {
         if (w < wave) before += red[w];
         t += red[w];
     }
@@ -152,6 +203,7 @@ __device__ __forceinline__ float block_scan(float v, float *red, float &total) {
     return before + v;
 }
 
+template <int NT = kT>
 __device__ __forceinline__ int block_count_scan(int flag, int *redi, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t bal = __ballot(flag);
@@ -161,12 +213,34 @@ __device__ __forceinline__ int block_count_scan(int flag, int *redi, int &total)
     __syncthreads();
     int before = 0, t = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < (NT / kWave); ++w) {
         if (w < wave) before += redi[w];
         t += redi[w];
     }
     total = t;
     return before + below;  // exclusive rank of this thread's flag
+}
+
+// Inclusive block scan of one int per thread; total receives the block sum.
+template <int NT = kT>
+__device__ __forceinline__ int block_scan_int(int v, int *redi, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    __syncthreads();
+    if (lane == 63) redi[wave] = v;
+    __syncthreads();
+    int before = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < (NT / kWave); ++w) {
+        if (w < wave) before += redi[w];
+        t += redi[w];
+    }
+    total = t;
+    return before + v;
 }
 
 // Visits x = tid, tid + kT, ... < V in batches of kUB, loads first (indices
@@ -193,7 +267,8 @@ __device__ __forceinline__ void row_pass(const StochArgs &a, size_t lrow, const 
 // so each group of 8 is consecutive.  When V is a multiple of 8 every group
 // is one 16-byte load of bf16 logits (two of f32) and two of q; otherwise
 // the same entries are loaded one by one.  Reads past the row give zero.
-__device__ __forceinline__ int reg_x(int j) { return 8 * (static_cast<int>(threadIdx.x) + kT * (j >> 3)) + (j & 7); }
+template <int NT = kT>
+__device__ __forceinline__ int reg_x(int j) { return 8 * (static_cast<int>(threadIdx.x) + NT * (j >> 3)) + (j & 7); }
 template <int RJ>
 __device__ __forceinline__ void load_row_regs(const StochArgs &a, size_t lrow, float (&lv)[RJ], float (&qv)[RJ]) {
     static_assert(RJ % 8 == 0, "whole groups of 8 entries");
@@ -340,12 +415,13 @@ __device__ __forceinline__ void wave_pass(const StochArgs &a, const RowRes &r, b
 }
 
 // parent slot of every slot of request b (-1 for roots), into LDS
+template <int NT = kT>
 __device__ __forceinline__ void build_parents(const StochArgs &a, int b, int n, int *parent) {
     const int P = a.W * a.L;
     const int32_t *un = a.unpacker + static_cast<size_t>(b) * P;
-    for (int i = threadIdx.x; i < P; i += kT) parent[i] = -1;
+    for (int i = threadIdx.x; i < P; i += NT) parent[i] = -1;
     __syncthreads();
-    for (int i = threadIdx.x; i < P; i += kT) {
+    for (int i = threadIdx.x; i < P; i += NT) {
         const int l = i % a.L;
         const int c = un[i];
         if (l > 0 && c >= 0 && c < n) parent[c] = un[i - 1];
@@ -354,48 +430,61 @@ __device__ __forceinline__ void build_parents(const StochArgs &a, int b, int n, 
 }
 
 // children of slot u in slot order into kids (at most kMaxBeams); returns their count
+template <int NT = kT>
 __device__ __forceinline__ int children_of(int u, int n, const int *parent, int *kids, int *redi, int *cnt_sh) {
-    const int cs = threadIdx.x;
-    const int flag = (cs > u && cs < n && parent[cs] == u) ? 1 : 0;
-    int tot;
-    const int r = block_count_scan(flag, redi, tot);
-    if (flag && r < kMaxBeams) kids[r] = cs;
-    if (threadIdx.x == 0) *cnt_sh = min(tot, kMaxBeams);
+    int carry = 0;
+    for (int c0 = 0; c0 < n; c0 += NT) {
+        const int cs = c0 + static_cast<int>(threadIdx.x);
+        const int flag = (cs > u && cs < n && parent[cs] == u) ? 1 : 0;
+        int tot;
+        const int r = carry + block_count_scan<NT>(flag, redi, tot);
+        if (flag && r < kMaxBeams) kids[r] = cs;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) *cnt_sh = min(carry, kMaxBeams);
     __syncthreads();
     return *cnt_sh;
 }
 
 // Bonus of a register-resident row: thread t holds p0 and q of its entries
 // x = reg_x(j) in pv[j], qv[j] (zeros past the row), so the weight of x is
-// max(pv[j] - c qv[j], 0).  The row is RJ/8 groups of 8*kT consecutive
+// max(pv[j] - c qv[j], 0).  The row is RJ/8 groups of 8*NT consecutive
 // entries.  The group holding the crossing of u_b times the total is found
 // from the groups' sums, then the thread by a block scan of the threads' sums
 // in that group, then the entry among the thread's 8.  When rounding between
 // the levels hides the crossing, the last entry of nonzero weight of the
 // chosen group (or thread) stands in, where the crossing lies in exact
 // arithmetic.  Returns the index in every thread.
-template <int RJ>
+// With have, tsk holds this thread's group sums of the weights for this c
+// already (from the residual pass that set c); otherwise they are formed
+// here.  gsum is 16-byte aligned.
+template <int RJ, int NT = kT>
 __device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&qv)[RJ], float c, float u_b,
-                                          float *red, int *redi, float *gsum) {
+                                          float *red, int *redi, float *gsum, const float (&tsk)[RJ / 8],
+                                          bool have) {
     constexpr int RG = RJ / 8;
+    constexpr int NW = NT / kWave;
+    static_assert(NW % 4 == 0, "group sums are read four at a time");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float w[RJ];
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) w[j] = fmaxf(pv[j] - c * qv[j], 0.f);
+    // weights are recomputed where needed rather than held (registers)
+    auto w = [&](int j) { return fmaxf(pv[j] - c * qv[j], 0.f); };
     float ts[RG];  // this thread's sum in each group
+    if (have) {
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        ts[g] = 0.f;
+        for (int g = 0; g < RG; ++g) ts[g] = tsk[g];
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ts[g] += w[8 * g + e];
+        for (int g = 0; g < RG; ++g) {
+            ts[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ts[g] += w(8 * g + e);
+        }
     }
     // group sums: per wave, then the waves in index order
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-        float v = ts[g];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
-        if (lane == 0) gsum[g * kNW + wave] = v;
+        const float v = wave_sum(ts[g]);
+        if (lane == 0) gsum[g * (NT / kWave) + wave] = v;
     }
     __syncthreads();
     float S[RG], total = 0.f;
@@ -403,7 +492,13 @@ __device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&q
     for (int g = 0; g < RG; ++g) {
         S[g] = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < kNW; ++w2) S[g] += gsum[g * kNW + w2];
+        for (int w4 = 0; w4 < NW / 4; ++w4) {
+            const float4 f = *reinterpret_cast<const float4 *>(gsum + g * NW + 4 * w4);
+            S[g] += f.x;
+            S[g] += f.y;
+            S[g] += f.z;
+            S[g] += f.w;
+        }
         total += S[g];
     }
     const float thr = u_b * total;
@@ -425,23 +520,29 @@ __device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&q
     for (int g = 0; g < RG; ++g)
         if (g == gs) mine = ts[g];
     float tot;
-    const float inc = block_scan(mine, red, tot);
+    const float inc = block_scan<NT>(mine, red, tot);
     const uint64_t hit = __ballot(exact && E + inc > thr);
     const uint64_t nz = __ballot(mine > 0.f);
     if (lane == 0) {
-        redi[wave] = hit ? wave * 64 + __ffsll(static_cast<long long>(hit)) - 1 : kT;
-        redi[kNW + wave] = nz ? wave * 64 + 63 - __clzll(static_cast<long long>(nz)) : -1;
+        redi[wave] = hit ? wave * 64 + __ffsll(static_cast<long long>(hit)) - 1 : NT;
+        redi[(NT / kWave) + wave] = nz ? wave * 64 + 63 - __clzll(static_cast<long long>(nz)) : -1;
     }
     __syncthreads();
-    int first = kT, last = -1;
+    int first = NT, last = -1;
 #pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) {
+    for (int w2 = 0; w2 < (NT / kWave); ++w2) {
         first = min(first, redi[w2]);
-        last = max(last, redi[kNW + w2]);
+        last = max(last, redi[(NT / kWave) + w2]);
     }
-    const int tsel = first < kT ? first : max(last, 0);
+    const int tsel = first < NT ? first : max(last, 0);
     // the entry among the chosen thread's 8 (its running sum from E + its exclusive prefix)
     if (static_cast<int>(threadIdx.x) == tsel) {
+        // the same weights again, from a copy of c the compiler cannot see
+        // through: merged with the ones summed above, all RJ would be held
+        // across the block scan
+        float c2 = c;
+        asm volatile("" : "+v"(c2));
+        auto w2 = [&](int j) { return fmaxf(pv[j] - c2 * qv[j], 0.f); };
         float r = E + (inc - mine);
         int es = -1, enz = 0;
 #pragma unroll
@@ -449,15 +550,23 @@ __device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&q
             if (g == gs) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    r += w[8 * g + e];
-                    if (es < 0 && first < kT && r > thr) es = e;
-                    if (w[8 * g + e] > 0.f) enz = e;
+                    const float we = w2(8 * g + e);
+                    r += we;
+                    if (es < 0 && first < NT && r > thr) es = e;
+                    if (we > 0.f) enz = e;
                 }
             }
-        redi[2 * kNW] = 8 * (tsel + kT * gs) + (es >= 0 ? es : enz);
+        redi[2 * (NT / kWave)] = 8 * (tsel + NT * gs) + (es >= 0 ? es : enz);
     }
     __syncthreads();
-    return redi[2 * kNW];
+    return redi[2 * (NT / kWave)];
+}
+
+template <int RJ, int NT = kT>
+__device__ __forceinline__ int bonus_regs(const float (&pv)[RJ], const float (&qv)[RJ], float c, float u_b,
+                                          float *red, int *redi, float *gsum) {
+    const float none[RJ / 8] = {};
+    return bonus_regs<RJ, NT>(pv, qv, c, u_b, red, redi, gsum, none, false);
 }
 
 // Bonus of a streamed row (p0 = exp(l - M) * invS, weight max(p0 - c q, 0)):
@@ -652,7 +761,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     __shared__ float red[2 * kNW];
     __shared__ int redi[2 * kNW + 1];
     __shared__ int tok_sh[kMaxSlots];
-    __shared__ float gsum[(RJ > 0 ? RJ / 8 : 1) * kNW];
+    __shared__ __attribute__((aligned(16))) float gsum[(RJ > 0 ? RJ / 8 : 1) * kNW];
     __shared__ int nkids_sh;
     __shared__ float wtot[kNW];  // streamed rows: per-wavefront weight sums for the bonus
     const int W = a.W, L = a.L, V = a.V;
@@ -778,6 +887,230 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     if (threadIdx.x == 0) a.bonus[ubase + u] = min(bonus, V - 1);
 }
 
+// Register-resident rows of bf16 logits with V a multiple of 8, in
+// persistent workgroups.  Each workgroup walks a contiguous range of the
+// valid slots in (request, slot) order and, while it computes slot r, has
+// slot r+1's loads in flight: its logits into registers (16-byte groups of
+// 8 entries, as load_row_regs), its q into LDS by direct loads (chunk c of
+// thread t at bytes (c*kRowT + t)*16, so every thread reads back its own
+// entries without bank conflicts), and the logit and q of its children's
+// tokens.  A row (192 KB at V = 32000) takes about as long to arrive at one
+// CU's share of the HBM bandwidth as its statistics take to compute, so one
+// workgroup per slot spent half its time waiting; here the two overlap.  A
+// request's parent array is built once per workgroup, not once per slot.
+// 512 threads of 64 entries each: the current row (p0 and q), the next
+// row's logits and the statistics fit the 256 registers of two wavefronts
+// per SIMD.  The statistics are those of k_stoch_node<32> over eight
+// wavefronts instead of sixteen.
+constexpr int kRowT = 512;               // threads per workgroup
+constexpr int kRowNW = kRowT / kWave;    // wavefronts
+constexpr int kRJ = 64;                  // entries per thread: rows of up to kRowT*kRJ
+struct RowsShared {
+    // the small arrays first: their addresses then fit the 16-bit offset
+    // field of LDS instructions instead of being held in registers
+    float2 cd_sh[kMaxBeams];
+    float red[2 * kRowNW];
+    int redi[2 * kRowNW + 1];
+    __attribute__((aligned(16))) float gsum[(kRJ / 8) * kRowNW];
+    int kids[kMaxBeams];
+    int nkids_sh;
+    int loc_sh[2];
+    int parent[kMaxSlots];
+    int tok_sh[kMaxSlots];
+    __attribute__((aligned(1024))) float qst[kRJ * kRowT];  // q of the next slot
+};
+__global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
+    __shared__ RowsShared sm;
+    float2 *const cd_sh = sm.cd_sh;
+    float *const red = sm.red;
+    int *const redi = sm.redi;
+    float *const gsum = sm.gsum;
+    int *const kids = sm.kids;
+    int &nkids_sh = sm.nkids_sh;
+    int *const loc_sh = sm.loc_sh;
+    int *const parent = sm.parent;
+    int *const tok_sh = sm.tok_sh;
+    float *const qst = sm.qst;
+    constexpr int NT = kRowT;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int B = a.B, W = a.W, L = a.L, V = a.V;
+    const int P = W * L;
+    auto plen_of = [&](int bb) { return min(max(a.plen[bb], 0), P); };
+
+    // valid slots (u < packed_len[b]) numbered in (b, u) order; this
+    // workgroup takes numbers [R*w/G, R*(w+1)/G)
+    long long R = 0;
+    for (int b0 = 0; b0 < B; b0 += NT) {
+        const int bb = b0 + tid;
+        int tot;
+        block_scan_int<NT>(bb < B ? plen_of(bb) : 0, redi, tot);
+        R += tot;
+    }
+    const long long r0 = R * blockIdx.x / gridDim.x, r1 = R * (blockIdx.x + 1) / gridDim.x;
+    if (r0 >= r1) return;
+    {
+        long long carry = 0;
+        for (int b0 = 0; b0 < B; b0 += NT) {
+            const int bb = b0 + tid;
+            const int n = bb < B ? plen_of(bb) : 0;
+            int tot;
+            const long long incl = carry + block_scan_int<NT>(n, redi, tot);
+            if (bb < B && incl - n <= r0 && r0 < incl) {
+                loc_sh[0] = bb;
+                loc_sh[1] = static_cast<int>(r0 - (incl - n));
+            }
+            carry += tot;
+        }
+        __syncthreads();
+    }
+    int b = __builtin_amdgcn_readfirstlane(loc_sh[0]);
+    int u = __builtin_amdgcn_readfirstlane(loc_sh[1]);
+    int n = plen_of(b);
+
+    // the request's tokens and parent array
+    auto load_request = [&](int bb, int nn) {
+        for (int i = tid; i < nn; i += NT) tok_sh[i] = a.ptok[static_cast<size_t>(bb) * P + i];
+        build_parents<NT>(a, bb, nn, parent);  // its barriers also publish tok_sh
+    };
+    // slot (bb, uu)'s loads, the logit (raw bf16 bits) and q of child kidn's
+    // token, and its bonus uniform.  Every load here is consumed only at the
+    // next slot's top: converting the logit now, or loading it only in the
+    // threads with a child (a merge of old and new values), would make the
+    // compiler wait for it -- and so for every load issued before it.
+    auto issue = [&](int bb, int uu, int kidn, u32x4 (&lr)[kRJ / 8], uint32_t &klr_o, float &kq_o, float &ub_o) {
+        const size_t lrow = (static_cast<size_t>(bb) * P + uu) * static_cast<size_t>(V);
+        // the lane's byte offsets are formed here from one opaque base: hoisted
+        // out of the loop, two dozen of them would be held in registers
+        uint32_t t16 = static_cast<uint32_t>(tid) * 16u;
+        asm volatile("" : "+v"(t16));
+        const rsrc_t rl = make_rsrc(static_cast<const uint16_t *>(a.logits) + lrow, static_cast<uint32_t>(V) * 2u);
+#pragma unroll
+        for (int g = 0; g < kRJ / 8; ++g)
+            lr[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, t16 + static_cast<uint32_t>(NT * g) * 16u, 0, 0);
+        const i32x4_t rq = make_srsrc(a.q + lrow, static_cast<uint32_t>(V) * 4u);
+        const uint32_t qdst = lds_addr_of(qst) + wave * 1024;
+#pragma unroll
+        for (int g = 0; g < kRJ / 8; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                lds_dma16(qdst + (2 * g + h) * NT * 16, rq, 2u * t16 + static_cast<uint32_t>(NT * g) * 32u + 16u * h);
+        const int x = min(max(tok_sh[max(kidn, 0)], 0), V - 1);
+        klr_o = static_cast<const uint16_t *>(a.logits)[lrow + x];
+        kq_o = a.q[lrow + x];
+        ub_o = a.u_bonus[bb];
+    };
+
+    load_request(b, n);
+    int nk = children_of<NT>(u, n, parent, kids, redi, &nkids_sh);
+    int kid = tid < nk ? kids[tid] : -1;
+    u32x4 lr[kRJ / 8];
+    uint32_t klr;
+    float kq, ub;
+    issue(b, u, kid, lr, klr, kq, ub);
+
+    for (long long r = r0; r < r1; ++r) {
+        // slot r's loads have landed (every thread's share, after the barrier)
+        vm_wait<0>();
+        __syncthreads();
+        float pv[kRJ], qv[kRJ];  // logits, then p0, and q of this thread's entries x = reg_x<NT>(j)
+        // V is a multiple of 8, so each 8-entry group lies wholly inside or
+        // wholly past the row: the logits of groups past it are set to -inf
+        // (p0 = 0 there, no masks below); q past the row reads as zero
+#pragma unroll
+        for (int g = 0; g < kRJ / 8; ++g) {
+            const bool gin = reg_x<NT>(8 * g) < V;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t wv = gin ? lr[g][k] : 0xFF80FF80u;
+                pv[8 * g + 2 * k] = __uint_as_float(wv << 16);
+                pv[8 * g + 2 * k + 1] = __uint_as_float(wv & 0xFFFF0000u);
+            }
+            const float4 q0 = *reinterpret_cast<const float4 *>(qst + ((2 * g) * NT + tid) * 4);
+            const float4 q1 = *reinterpret_cast<const float4 *>(qst + ((2 * g + 1) * NT + tid) * 4);
+            qv[8 * g + 0] = q0.x;
+            qv[8 * g + 1] = q0.y;
+            qv[8 * g + 2] = q0.z;
+            qv[8 * g + 3] = q0.w;
+            qv[8 * g + 4] = q1.x;
+            qv[8 * g + 5] = q1.y;
+            qv[8 * g + 6] = q1.z;
+            qv[8 * g + 7] = q1.w;
+        }
+        // slot r's values, held while slot r+1's loads go out (the asm keeps
+        // the compiler from waiting for them later, behind the new loads)
+        const int cb = b, cu = u, cnk = nk, ckid = kid;
+        float ckq = kq, cub = ub;
+        uint32_t cklr = klr;
+        asm volatile("" : "+v"(cklr), "+v"(ckq), "+v"(cub));
+        const float ckl = __uint_as_float(cklr << 16);
+        __syncthreads();  // every thread has read q from LDS
+        if (r + 1 < r1) {
+            if (++u >= n) {
+                do {
+                    ++b;
+                    n = plen_of(b);
+                } while (n == 0);
+                u = 0;
+                load_request(b, n);
+            }
+            nk = children_of<NT>(u, n, parent, kids, redi, &nkids_sh);
+            kid = tid < nk ? kids[tid] : -1;
+            issue(b, u, kid, lr, klr, kq, ub);
+        }
+
+        // slot r: softmax statistics from registers
+        const size_t ubase = static_cast<size_t>(cb) * P;
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) m = fmaxf(m, pv[j]);
+        const float M = block_max<NT>(m, red);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) {
+            pv[j] = __expf(pv[j] - M);
+            s += pv[j];
+        }
+        const float invS = 1.f / block_sum<NT>(s, red);
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) pv[j] *= invS;
+        if (tid == 0) cd_sh[0] = make_float2(0.f, 1.f);
+        // each pass keeps its per-group sums: when the last pass sets c they
+        // are the bonus weights' group sums already
+        float c = 0.f, D = 1.f;
+        float tsk[kRJ / 8];
+        bool have = false;
+        for (int i = 0; i < cnk; ++i) {
+            const float cn = c + D;
+            float t = 0.f;
+#pragma unroll
+            for (int g = 0; g < kRJ / 8; ++g) {
+                float tg = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tg += fmaxf(pv[8 * g + e] - cn * qv[8 * g + e], 0.f);
+                tsk[g] = tg;
+                t += tg;
+            }
+            const float T = block_sum<NT>(t, red);
+            have = T > 0.f;
+            if (have) {
+                c = cn;
+                D = T;
+            }
+            if (tid == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
+        }
+        __syncthreads();
+        if (ckid >= 0) {
+            const float2 cd = cd_sh[tid];
+            const float px = fmaxf(__expf(ckl - M) * invS - cd.x * ckq, 0.f) / cd.y;
+            a.test[ubase + ckid] = make_float2(px, ckq);
+        }
+        const int bonus = bonus_regs<kRJ, NT>(pv, qv, c, cub, red, redi, gsum, tsk, have);
+        if (tid == 0) a.bonus[ubase + cu] = min(bonus, V - 1);
+    }
+    vm_wait<0>();
+}
+
 __global__ __launch_bounds__(kT) void k_stoch_walk(StochArgs a) {
     __shared__ int parent[kMaxSlots];
     __shared__ float2 test_sh[kMaxSlots];  // (p_i(x), q(x)) of each slot's test at its parent
@@ -852,11 +1185,16 @@ hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const in
                                     const void *logits, const float *q, const float *u_accept, const float *u_bonus,
                                     int B, int W, int L, int V, int32_t *best_beam, int32_t *accept_len,
                                     int32_t *accepted, int32_t *path, void *ws, hipStream_t stream) {
-    StochArgs a{unpacker, plen, ptok, logits, q, u_accept, u_bonus, W, L, V, dtype == 1 ? 1 : 0,
+    StochArgs a{unpacker, plen, ptok, logits, q, u_accept, u_bonus, B, W, L, V, dtype == 1 ? 1 : 0,
                 best_beam, accept_len, accepted, path, static_cast<float2 *>(ws),
                 reinterpret_cast<int32_t *>(static_cast<float2 *>(ws) + static_cast<size_t>(B) * W * L)};
-    const dim3 grid(static_cast<unsigned>(static_cast<size_t>(B) * W * L));
-    if (V <= kT * 32)
+    const size_t slots = static_cast<size_t>(B) * W * L;
+    const dim3 grid(static_cast<unsigned>(slots));
+    if (dtype == 1 && V % 8 == 0 && V <= kRowT * kRJ) {
+        // persistent: one workgroup per CU (fewer when there are fewer slots)
+        const unsigned g = static_cast<unsigned>(std::min<size_t>(slots, static_cast<size_t>(device_cu_count())));
+        hipLaunchKernelGGL(k_stoch_rows, dim3(g), dim3(kRowT), 0, stream, a);
+    } else if (V <= kT * 32)
         hipLaunchKernelGGL(k_stoch_node<32>, grid, dim3(kT), 0, stream, a);
     else if (V % 8 == 0)
         hipLaunchKernelGGL(k_stoch_node<-1>, grid, dim3(kT), 0, stream, a);
