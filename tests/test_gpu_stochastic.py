@@ -152,3 +152,53 @@ def test_peaked_targets_match_the_greedy_accept():
         assert torch.equal(got[key], greedy[key]), key
     assert int(greedy["accept_len"].max()) > 0
     say(f"[stochastic] peaked: accept lengths {greedy['accept_len'].tolist()}")
+
+
+def test_stochastic_empty_requests_between_full_ones():
+    """Requests with no packed slots (the first, the last and two adjacent ones) between full ones.
+
+    With bf16 logits and V a multiple of 8 the slots are split into contiguous
+    ranges of the valid ones, one range per workgroup, each range spanning
+    several slots here: a range that reaches an empty request must skip it.
+    Empty requests give -1 everywhere, as in the oracle.
+    """
+    B, W, L, V = 7, 64, 8, 4096
+    empty = [0, 2, 3, 6]
+    cfg = get_config("llama_mha").with_(B=B, W=W, L=L, V=V)
+    beams = draw_beams(cfg, base_seed(cfg, 8))
+    beams[:, :, 0] = beams[:, :1, 0]
+    beams = beams % V
+    P = W * L
+    rng = np.random.default_rng(131)
+    logits = round_to_bf16((rng.standard_normal((B, P, V)) * 2.5).astype(np.float32))
+    q = (0.8 * softmax(logits.astype(np.float64)) + 0.2 * softmax(rng.standard_normal((B, P, V)) * 2.5)).astype(
+        np.float32)
+    pk = oracle.pack_beams(beams)
+    for b in empty:
+        pk["length"][b] = 0
+        pk["unpacker"][b] = -1
+        pk["tokens"][b] = -1
+    ua = np.zeros((B, L, W), np.float32)
+    ub = np.zeros(B, np.float32)
+    for b in range(B):
+        if b in empty:
+            ua[b], ub[b] = rng.random((L, W)), rng.random()
+            continue
+        sl = slice(b, b + 1)
+        pk_b = {k: v[sl] for k, v in pk.items()}
+        a_, b_, _ = robust_uniforms(beams[sl], pk_b, logits[sl].astype(np.float64), q[sl].astype(np.float64),
+                                     rng, W, L)
+        ua[b], ub[b] = a_[0], b_[0]
+    ua = ua.astype(np.float32)
+    ub = ub.astype(np.float32)
+    say(f"[stochastic] empty requests {empty}: packed lengths {pk['length'].tolist()}")
+    got = rd.rd_stochastic_accept(dev_int(pk["unpacker"]), dev_int(pk["length"]), dev_int(pk["tokens"]),
+                                  torch.from_numpy(logits).cuda().to(torch.bfloat16), torch.from_numpy(q).cuda(),
+                                  torch.from_numpy(ua).cuda(), torch.from_numpy(ub).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.stochastic_accept(beams, pk["unpacker"], pk["length"], pk["tokens"], logits.astype(np.float64),
+                                   q.astype(np.float64), ua.astype(np.float64), ub.astype(np.float64))
+    for key in ("accept_len", "best_beam", "accepted_tokens", "path"):
+        np.testing.assert_array_equal(got[key].cpu().numpy(), ref[key], err_msg=key)
+    assert (ref["accept_len"][empty] == -1).all()
+    say(f"[stochastic] accept lengths {ref['accept_len'].tolist()}")
