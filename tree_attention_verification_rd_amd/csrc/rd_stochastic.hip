@@ -973,8 +973,8 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
         for (int i = tid; i < nn; i += NT) tok_sh[i] = a.ptok[static_cast<size_t>(bb) * P + i];
         build_parents<NT>(a, bb, nn, parent);  // its barriers also publish tok_sh
     };
-    // slot (bb, uu)'s loads, the logit (raw bf16 bits) and q of child kidn's
-    // token, and its bonus uniform.  Every load here is consumed only at the
+    // slot (bb, uu)'s logits into registers, the logit (raw bf16 bits) and q
+    // of child kidn's token, and its bonus uniform.  Every load here is consumed only at the
     // next slot's top: converting the logit now, or loading it only in the
     // threads with a child (a merge of old and new values), would make the
     // compiler wait for it -- and so for every load issued before it.
@@ -988,19 +988,29 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
 #pragma unroll
         for (int g = 0; g < kRJ / 8; ++g)
             lr[g] = __builtin_amdgcn_raw_buffer_load_b128(rl, t16 + static_cast<uint32_t>(NT * g) * 16u, 0, 0);
-        const i32x4_t rq = make_srsrc(a.q + lrow, static_cast<uint32_t>(V) * 4u);
-        const uint32_t qdst = lds_addr_of(qst) + wave * 1024;
-#pragma unroll
-        for (int g = 0; g < kRJ / 8; ++g)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                lds_dma16(qdst + (2 * g + h) * NT * 16, rq, 2u * t16 + static_cast<uint32_t>(NT * g) * 32u + 16u * h);
         const int x = min(max(tok_sh[max(kidn, 0)], 0), V - 1);
         klr_o = static_cast<const uint16_t *>(a.logits)[lrow + x];
         kq_o = a.q[lrow + x];
         ub_o = a.u_bonus[bb];
     };
 
+    // quarter hh of slot (bb, uu)'s q, by direct loads into LDS.  The
+    // quarters go out at four points of the current slot's statistics: issued
+    // together with the rest (24 wide loads per thread) they held each
+    // wavefront at the load issue long enough to delay those statistics
+    // (dedup sweep p = 0.1: 1292 -> 1131 us).
+    auto issue_q = [&](int bb, int uu, int hh) {
+        const size_t lrow = (static_cast<size_t>(bb) * P + uu) * static_cast<size_t>(V);
+        uint32_t t16 = static_cast<uint32_t>(tid) * 16u;
+        asm volatile("" : "+v"(t16));
+        const i32x4_t rq = make_srsrc(a.q + lrow, static_cast<uint32_t>(V) * 4u);
+        const uint32_t qdst = lds_addr_of(qst) + wave * 1024;
+#pragma unroll
+        for (int g = hh * (kRJ / 32); g < (hh + 1) * (kRJ / 32); ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                lds_dma16(qdst + (2 * g + h) * NT * 16, rq, 2u * t16 + static_cast<uint32_t>(NT * g) * 32u + 16u * h);
+    };
     load_request(b, n);
     int nk = children_of<NT>(u, n, parent, kids, redi, &nkids_sh);
     int kid = tid < nk ? kids[tid] : -1;
@@ -1008,6 +1018,10 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
     uint32_t klr;
     float kq, ub;
     issue(b, u, kid, lr, klr, kq, ub);
+    issue_q(b, u, 0);
+    issue_q(b, u, 1);
+    issue_q(b, u, 2);
+    issue_q(b, u, 3);
 
     for (long long r = r0; r < r1; ++r) {
         // slot r's loads have landed (every thread's share, after the barrier)
@@ -1019,7 +1033,9 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
         // (p0 = 0 there, no masks below); q past the row reads as zero
 #pragma unroll
         for (int g = 0; g < kRJ / 8; ++g) {
-            const bool gin = reg_x<NT>(8 * g) < V;
+            // group g lies inside the row for every thread when 8*NT*(g+1) <= V
+            // (a uniform test): only the groups reaching past V are masked
+            const bool gin = 8 * NT * (g + 1) <= V || reg_x<NT>(8 * g) < V;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t wv = gin ? lr[g][k] : 0xFF80FF80u;
@@ -1065,13 +1081,18 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) m = fmaxf(m, pv[j]);
         const float M = block_max<NT>(m, red);
+        if (r + 1 < r1) issue_q(b, u, 0);
+        // exp(l - M) as 2^(l log2(e) - M log2(e)): one multiply-add, no subtraction
+        // (v_exp_f32 as __expf uses it: results below the normal range flush to 0)
+        const float ML = M * kLog2e;
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) {
-            pv[j] = __expf(pv[j] - M);
+            pv[j] = fast_exp2(fmaf(pv[j], kLog2e, -ML));
             s += pv[j];
         }
         const float invS = 1.f / block_sum<NT>(s, red);
+        if (r + 1 < r1) issue_q(b, u, 1);
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) pv[j] *= invS;
         if (tid == 0) cd_sh[0] = make_float2(0.f, 1.f);
@@ -1100,11 +1121,13 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
             if (tid == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
         }
         __syncthreads();
+        if (r + 1 < r1) issue_q(b, u, 2);
         if (ckid >= 0) {
             const float2 cd = cd_sh[tid];
-            const float px = fmaxf(__expf(ckl - M) * invS - cd.x * ckq, 0.f) / cd.y;
+            const float px = fmaxf(fast_exp2(fmaf(ckl, kLog2e, -ML)) * invS - cd.x * ckq, 0.f) / cd.y;
             a.test[ubase + ckid] = make_float2(px, ckq);
         }
+        if (r + 1 < r1) issue_q(b, u, 3);
         const int bonus = bonus_regs<kRJ, NT>(pv, qv, c, cub, red, redi, gsum, tsk, have);
         if (tid == 0) a.bonus[ubase + cu] = min(bonus, V - 1);
     }
