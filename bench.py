@@ -466,6 +466,13 @@ def main():
                                         path=s_path, workspace=s_ws, **s_out)
 
             stoch_us = queued_call_us(stoch_call, lambda: None)
+        # bytes the call must read: the logits and q rows of every valid slot
+        # (the tree structure, uniforms and outputs are a few hundred KB)
+        stoch_entry = {"call": "rd_stochastic_accept", "avg_us": None if stoch_us is None else round(stoch_us, 2)}
+        if stoch_us is not None:
+            sbytes = int(pk["length"].sum().item()) * cfg.V * (esz + 4)
+            stoch_entry.update({"hbm_bytes": sbytes, "tb_per_s": round(sbytes / stoch_us / 1e6, 3),
+                                "frac_of_8tbps": round(sbytes / stoch_us / 1e6 / 8.0, 3)})
 
         ragged_pack_us = queued_call_us(ragged_pack_call, lambda: None)
         ragged_accept_us = queued_call_us(ragged_accept_call, lambda: None)
@@ -479,8 +486,7 @@ def main():
             "separate_gather_us": None if gather_us is None else round(gather_us, 2),
             "after_step": {"call": "rd_commit_accepted", "accept_len": cfg.L - 1, "avg_us": round(commit_us, 2),
                            "paged_avg_us": round(commit_paged_us, 2), "bytes_moved": int(commit_bytes)},
-            "stochastic": {"call": "rd_stochastic_accept",
-                           "avg_us": None if stoch_us is None else round(stoch_us, 2)},
+            "stochastic": stoch_entry,
             "ragged": {"calls": "rd_pack_beams_mask_ragged + rd_unpack_accept_ragged",
                        "candidates": int((r_bw * r_bl).sum().item()), "packed_tokens": ragged_packed,
                        "pack_mask_us": round(ragged_pack_us, 2), "unpack_accept_us": round(ragged_accept_us, 2)},
