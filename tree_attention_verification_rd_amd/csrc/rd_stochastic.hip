@@ -995,10 +995,12 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
     };
 
     // quarter hh of slot (bb, uu)'s q, by direct loads into LDS.  The
-    // quarters go out at four points of the current slot's statistics: issued
-    // together with the rest (24 wide loads per thread) they held each
+    // quarters go out at four points of the current slot's statistics (with
+    // the logits, after the max, after the sum, after the residual passes):
+    // issued together with the rest (24 wide loads per thread) they held each
     // wavefront at the load issue long enough to delay those statistics
-    // (dedup sweep p = 0.1: 1292 -> 1131 us).
+    // (dedup sweep p = 0.1: 1292 -> 1131 us; the last quarter before the
+    // bonus search rather than after it: 1103 us).
     auto issue_q = [&](int bb, int uu, int hh) {
         const size_t lrow = (static_cast<size_t>(bb) * P + uu) * static_cast<size_t>(V);
         uint32_t t16 = static_cast<uint32_t>(tid) * 16u;
@@ -1073,6 +1075,7 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
             nk = children_of<NT>(u, n, parent, kids, redi, &nkids_sh);
             kid = tid < nk ? kids[tid] : -1;
             issue(b, u, kid, lr, klr, kq, ub);
+            issue_q(b, u, 0);
         }
 
         // slot r: softmax statistics from registers
@@ -1081,7 +1084,7 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) m = fmaxf(m, pv[j]);
         const float M = block_max<NT>(m, red);
-        if (r + 1 < r1) issue_q(b, u, 0);
+        if (r + 1 < r1) issue_q(b, u, 1);
         // exp(l - M) as 2^(l log2(e) - M log2(e)): one multiply-add, no subtraction
         // (v_exp_f32 as __expf uses it: results below the normal range flush to 0)
         const float ML = M * kLog2e;
@@ -1092,7 +1095,7 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
             s += pv[j];
         }
         const float invS = 1.f / block_sum<NT>(s, red);
-        if (r + 1 < r1) issue_q(b, u, 1);
+        if (r + 1 < r1) issue_q(b, u, 2);
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) pv[j] *= invS;
         if (tid == 0) cd_sh[0] = make_float2(0.f, 1.f);
@@ -1121,13 +1124,12 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
             if (tid == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
         }
         __syncthreads();
-        if (r + 1 < r1) issue_q(b, u, 2);
+        if (r + 1 < r1) issue_q(b, u, 3);
         if (ckid >= 0) {
             const float2 cd = cd_sh[tid];
             const float px = fmaxf(fast_exp2(fmaf(ckl, kLog2e, -ML)) * invS - cd.x * ckq, 0.f) / cd.y;
             a.test[ubase + ckid] = make_float2(px, ckq);
         }
-        if (r + 1 < r1) issue_q(b, u, 3);
         const int bonus = bonus_regs<kRJ, NT>(pv, qv, c, cub, red, redi, gsum, tsk, have);
         if (tid == 0) a.bonus[ubase + cu] = min(bonus, V - 1);
     }
