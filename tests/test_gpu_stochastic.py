@@ -70,6 +70,8 @@ CASES = {
     "big_vocab_f32": (2, 3, 4, 36000, "f32", 2.5, 0.8),  # streamed 16-byte groups of f32 logits
     "big_vocab_odd": (2, 3, 4, 40003, "bf16", 2.5, 0.8),  # not a multiple of 8: streamed entry by entry
     "vocab_128k": (1, 4, 3, 128256, "bf16", 3.0, 0.9),    # the 128256-entry vocabulary of the GQA workloads
+    "vocab_32768": (2, 4, 4, 32768, "bf16", 2.5, 0.8),    # the largest register-resident row: no group past the row
+    "vocab_32776": (2, 4, 4, 32776, "bf16", 2.5, 0.8),    # one 8-entry group more: streamed passes
 }
 
 
