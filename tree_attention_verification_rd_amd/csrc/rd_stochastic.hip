@@ -142,6 +142,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // softmax: two pairs merge as M = max, s = s1 e^(m1-M) + s2 e^(m2-M)).
 // red is LDS scratch of 2 kNW floats.  Returns M; S in *S.
 __device__ __forceinline__ float merge_scale(float m, float M) { return m == -INFINITY ? 0.f : __expf(m - M); }
+template <int NT = kT>
 __device__ __forceinline__ float block_softmax_stats(float m, float s, float *red, float *S) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -153,15 +154,15 @@ __device__ __forceinline__ float block_softmax_stats(float m, float s, float *re
     __syncthreads();
     if ((threadIdx.x & 63) == 0) {
         red[threadIdx.x >> 6] = m;
-        red[kNW + (threadIdx.x >> 6)] = s;
+        red[(NT / kWave) + (threadIdx.x >> 6)] = s;
     }
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, red[w]);
+    for (int w = 0; w < (NT / kWave); ++w) M = fmaxf(M, red[w]);
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) t += red[kNW + w] * merge_scale(red[w], M);
+    for (int w = 0; w < (NT / kWave); ++w) t += red[(NT / kWave) + w] * merge_scale(red[w], M);
     *S = t;
     return M;
 }
@@ -392,8 +393,9 @@ __device__ __forceinline__ void unpack_grp(const StochArgs &a, const Grp &v, flo
 // sums).  A wavefront walks its range 64 groups (1 KB of bf16 logits) a
 // step, kSBV steps loaded together, calling f(l[8], q[8]) on each group.
 constexpr int kSBV = 4;
+template <int NT = kT>
 __device__ __forceinline__ void wave_range(int G, int &g0, int &g1) {
-    const int GW = (G + kNW - 1) / kNW;
+    const int GW = (G + (NT / kWave) - 1) / (NT / kWave);
     g0 = min(static_cast<int>(threadIdx.x >> 6) * GW, G);
     g1 = min(g0 + GW, G);
 }
@@ -669,6 +671,7 @@ __device__ __forceinline__ int bonus_streamed(const StochArgs &a, size_t lrow, c
 // entries of the crossing lane.  Where rounding between the levels hides
 // the crossing, the range's last entry of nonzero weight stands in.  Result
 // valid in every thread.
+template <int NT = kT>
 __device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowRes &r, float M, float invS, float c,
                                                   float u_b, const float *wtot, int *redi) {
     const int V = a.V;
@@ -676,12 +679,12 @@ __device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowR
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     float total = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) total += wtot[w2];
+    for (int w2 = 0; w2 < (NT / kWave); ++w2) total += wtot[w2];
     const float thr = u_b * total;
     int ws = -1, wlast = -1;
     float exc = 0.f, ews = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) {
+    for (int w2 = 0; w2 < (NT / kWave); ++w2) {
         if (ws < 0 && exc + wtot[w2] > thr) {
             ws = w2;
             ews = exc;
@@ -690,12 +693,12 @@ __device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowR
         exc += wtot[w2];
     }
     if (ws < 0) {  // rounding put the threshold at or past the total
-        ws = wlast >= 0 ? wlast : kNW - 1;
+        ws = wlast >= 0 ? wlast : (NT / kWave) - 1;
         ews = -INFINITY;  // never crosses: the range's last nonzero entry stands in
     }
     if (wv == ws) {
         int g0, g1;
-        wave_range(G, g0, g1);
+        wave_range<NT>(G, g0, g1);
         int cand = -1, lastnz = -1;
         float carry = ews;
         for (int s0 = 0; s0 < g1 - g0 && cand < 0; s0 += 64 * kSBV) {
@@ -753,17 +756,18 @@ __device__ __forceinline__ int bonus_streamed_vec(const StochArgs &a, const RowR
 // are loaded once into registers (element x = tid + kT*j) and every pass runs
 // on them; with RJ == 0 each pass streams the row entry by entry, with
 // RJ < 0 (V a multiple of 8) in 16-byte groups of 8 entries.
-template <int RJ>
-__global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
+template <int RJ, int NT = kT>
+__global__ __launch_bounds__(NT, kT / NT) void k_stoch_node(StochArgs a) {
+    static_assert(NT == kT || RJ < 0, "only the streamed 16-byte path runs with other workgroup sizes");
     __shared__ int parent[kMaxSlots];
     __shared__ int kids[kMaxBeams];
     __shared__ float2 cd_sh[kMaxBeams];
-    __shared__ float red[2 * kNW];
-    __shared__ int redi[2 * kNW + 1];
+    __shared__ float red[2 * (NT / kWave)];
+    __shared__ int redi[2 * (NT / kWave) + 1];
     __shared__ int tok_sh[kMaxSlots];
-    __shared__ __attribute__((aligned(16))) float gsum[(RJ > 0 ? RJ / 8 : 1) * kNW];
+    __shared__ __attribute__((aligned(16))) float gsum[(RJ > 0 ? RJ / 8 : 1) * (NT / kWave)];
     __shared__ int nkids_sh;
-    __shared__ float wtot[kNW];  // streamed rows: per-wavefront weight sums for the bonus
+    __shared__ float wtot[(NT / kWave)];  // streamed rows: per-wavefront weight sums for the bonus
     const int W = a.W, L = a.L, V = a.V;
     const int P = W * L;
     const int b = blockIdx.x / P;
@@ -775,12 +779,12 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     const float *qrow = a.q + lrow;
     const RowRes rr = row_res(a, lrow);
     int vg0 = 0, vg1 = 0;  // this wavefront's range of 8-entry groups (streamed rows)
-    if constexpr (RJ < 0) wave_range(V / 8, vg0, vg1);
+    if constexpr (RJ < 0) wave_range<NT>(V / 8, vg0, vg1);
     float pv[RJ > 0 ? RJ : 1], qv[RJ > 0 ? RJ : 1];  // logits, then p0, and q of this thread's elements
     if constexpr (RJ > 0) load_row_regs<RJ>(a, lrow, pv, qv);  // issued first: the loads overlap the tree build
-    if (static_cast<int>(threadIdx.x) < n) tok_sh[threadIdx.x] = a.ptok[ubase + threadIdx.x];
-    build_parents(a, b, n, parent);  // its barriers also publish tok_sh
-    const int nk = children_of(u, n, parent, kids, redi, &nkids_sh);
+    for (int i = threadIdx.x; i < n; i += NT) tok_sh[i] = a.ptok[ubase + i];
+    build_parents<NT>(a, b, n, parent);  // its barriers also publish tok_sh
+    const int nk = children_of<NT>(u, n, parent, kids, redi, &nkids_sh);
     // thread i < nk: child i's token, its logit and q (their latency hides
     // behind the softmax statistics)
     int kid = -1;
@@ -827,12 +831,12 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
             m = mn;
         });
         float S;
-        M = block_softmax_stats(m, s, red, &S);
+        M = block_softmax_stats<NT>(m, s, red, &S);
         invS = 1.f / S;
         // red holds each wavefront's merged (max, sum): its range's share of
         // p0, the bonus weights while c = 0
-        if (static_cast<int>(threadIdx.x) < kNW)
-            wtot[threadIdx.x] = red[kNW + threadIdx.x] * merge_scale(red[threadIdx.x], M) * invS;
+        if (static_cast<int>(threadIdx.x) < (NT / kWave))
+            wtot[threadIdx.x] = red[(NT / kWave) + threadIdx.x] * merge_scale(red[threadIdx.x], M) * invS;
     } else {
         float m = -INFINITY, s = 0.f;
         row_pass(a, lrow, nullptr, V, [&](int, float l, float) {
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
             m = mn;
         });
         float S;
-        M = block_softmax_stats(m, s, red, &S);
+        M = block_softmax_stats<NT>(m, s, red, &S);
         invS = 1.f / S;
     }
     if (threadIdx.x == 0) cd_sh[0] = make_float2(0.f, 1.f);
@@ -861,12 +865,12 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
             row_pass(a, lrow, qrow, V,
                      [&](int, float l, float q1) { t += fmaxf(__expf(l - M) * invS - cn * q1, 0.f); });
         }
-        const float T = block_sum(t, red);
+        const float T = block_sum<NT>(t, red);
         if (T > 0.f) {
             c = cn;
             D = T;
             // red holds the wavefronts' sums of max(p0 - c q, 0) for the new c
-            if (RJ < 0 && static_cast<int>(threadIdx.x) < kNW) wtot[threadIdx.x] = red[threadIdx.x];
+            if (RJ < 0 && static_cast<int>(threadIdx.x) < (NT / kWave)) wtot[threadIdx.x] = red[threadIdx.x];
         }
         if (threadIdx.x == 0 && i + 1 < kMaxBeams) cd_sh[i + 1] = make_float2(c, D);
     }
@@ -881,7 +885,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
     if constexpr (RJ > 0)
         bonus = bonus_regs<RJ>(pv, qv, c, ub, red, redi, gsum);
     else if constexpr (RJ < 0)
-        bonus = bonus_streamed_vec(a, rr, M, invS, c, ub, wtot, redi);
+        bonus = bonus_streamed_vec<NT>(a, rr, M, invS, c, ub, wtot, redi);
     else
         bonus = bonus_streamed(a, lrow, qrow, M, invS, c, ub, red, redi);
     if (threadIdx.x == 0) a.bonus[ubase + u] = min(bonus, V - 1);
@@ -905,6 +909,7 @@ __global__ __launch_bounds__(kT) void k_stoch_node(StochArgs a) {
 constexpr int kRowT = 512;               // threads per workgroup
 constexpr int kRowNW = kRowT / kWave;    // wavefronts
 constexpr int kRJ = 64;                  // entries per thread: rows of up to kRowT*kRJ
+constexpr int kStreamT = 512;            // threads per workgroup of the streamed 16-byte path
 struct RowsShared {
     // the small arrays first: their addresses then fit the 16-bit offset
     // field of LDS instructions instead of being held in registers
@@ -1222,7 +1227,9 @@ hipError_t launch_stochastic_accept(int dtype, const int32_t *unpacker, const in
     } else if (V <= kT * 32)
         hipLaunchKernelGGL(k_stoch_node<32>, grid, dim3(kT), 0, stream, a);
     else if (V % 8 == 0)
-        hipLaunchKernelGGL(k_stoch_node<-1>, grid, dim3(kT), 0, stream, a);
+        // 512 threads, two workgroups per CU: one workgroup's reductions and
+        // single-wavefront bonus scan overlap the other's streamed passes
+        hipLaunchKernelGGL((k_stoch_node<-1, kStreamT>), grid, dim3(kStreamT), 0, stream, a);
     else
         hipLaunchKernelGGL(k_stoch_node<0>, grid, dim3(kT), 0, stream, a);
     hipError_t e = hipGetLastError();
