@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="requests in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run a plain device copy of this size (a known-traffic reference for HBM counters)")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="'on' times the steps as replays of HIP graphs captured once per input set (the per-call "
+                         "durations, and so the rooflines, then come from as many eager steps after the timed "
+                         "region); 'off' (default) times eager calls with the per-call events inside the timed "
+                         "steps. A failed capture falls back to 'off' and says so in the JSON line")
     ap.add_argument("--legs", choices=["all", "step"], default="all",
                     help="'step' times the verification step only (no commit/paged/ragged/stochastic legs)")
     ap.add_argument("--peaks", action="store_true",
@@ -315,19 +320,54 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    # Timed region: K whole steps, bracketed by synchronisation.  A HIP event
-    # on the launch stream (torch's current stream, which the binding passes
-    # to every call) sits between consecutive calls, so the per-call
+    # The step captured once per input set in a HIP graph (every call takes
+    # torch's current stream and the preallocated buffers, and records no
+    # memset): a replay launches the same kernels without the host's
+    # per-call work and the gaps between launches.
+    graphs, graph_note = None, None
+    if args.graph == "on":
+        try:
+            graphs = []
+            for s_ in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(s_)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            graph_note = f"timed steps are replays of {len(graphs)} HIP graphs (one per input set)"
+        except Exception as exc:  # noqa: BLE001 -- any capture failure falls back to eager timing
+            graphs = None
+            graph_note = f"graph capture failed, eager steps timed: {type(exc).__name__}: {exc}"[:240]
+            torch.cuda.synchronize()
+    # Timed region: K whole steps, bracketed by synchronisation.  Eager: a HIP
+    # event on the launch stream (torch's current stream, which the binding
+    # passes to every call) sits between consecutive calls, so the per-call
     # durations come from the timed steps themselves; at this size each event
-    # costs the GPU a few microseconds of a step of milliseconds.
+    # costs the GPU a few microseconds of a step of milliseconds.  Graphs: the
+    # K replays are timed, and the per-call durations come from K eager steps
+    # with the events run after them.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(K):
-        step(sets[i % n_sets], evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_gpu = evs[0][0].elapsed_time(evs[K - 1][5]) / K
+    if graphs:
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        w0 = time.perf_counter()
+        ge[0].record()
+        for i in range(K):
+            graphs[i % n_sets].replay()
+        ge[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_gpu = ge[0].elapsed_time(ge[1]) / K
+        for i in range(K):
+            step(sets[i % n_sets], evs[i])
+        torch.cuda.synchronize()
+    else:
+        w0 = time.perf_counter()
+        for i in range(K):
+            step(sets[i % n_sets], evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_gpu = evs[0][0].elapsed_time(evs[K - 1][5]) / K
     ms_per_step = max(wall * 1e3 / K, ms_gpu)
     marks = {"pack_mask": (0, 2), "attention": (2, 3), "lm_head": (3, 4), "unpack_accept": (4, 5)}
     per_call_us = {n: float(np.mean([e[j0].elapsed_time(e[j1]) for e in evs]) * 1e3) for n, (j0, j1) in marks.items()}
@@ -546,6 +586,7 @@ def main():
                           "binding_roof_frac": round(binding_frac("attention"), 4)},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "gpu_ms_per_step": round(ms_gpu, 4),
+        "graph": bool(graphs), "timing": graph_note or "eager calls timed",
     }
     # The gather's roofline: the step's rd_unpack_accept, or, when the step
     # folds the gather into the projection, the separate call timed beside it
