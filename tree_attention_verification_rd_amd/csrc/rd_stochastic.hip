@@ -904,8 +904,11 @@ __global__ __launch_bounds__(NT, kT / NT) void k_stoch_node(StochArgs a) {
 // request's parent array is built once per workgroup, not once per slot.
 // 512 threads of 64 entries each: the current row (p0 and q), the next
 // row's logits and the statistics fit the 256 registers of two wavefronts
-// per SIMD.  The statistics are those of k_stoch_node<32> over eight
-// wavefronts instead of sixteen.
+// per SIMD.  The statistics are those of k_stoch_node<32>, with these
+// differences in how they are formed: block reductions over eight
+// wavefronts instead of sixteen; p0 = 2^(l log2(e) - M log2(e)) (one
+// multiply-add before the exponential); each residual pass keeps its
+// per-group sums, which the bonus search reuses when that pass set c.
 constexpr int kRowT = 512;               // threads per workgroup
 constexpr int kRowNW = kRowT / kWave;    // wavefronts
 constexpr int kRJ = 64;                  // entries per thread: rows of up to kRowT*kRJ
