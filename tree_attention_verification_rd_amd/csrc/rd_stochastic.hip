@@ -38,8 +38,8 @@
 //                    rescans only the range that holds the crossing.
 //                    Otherwise entry by entry, each wave taking a contiguous
 //                    range for the bonus;
-//   k_stoch_walk  -- one wavefront per request: the pairs and the request's
-//                    uniforms are staged in LDS; from slot 0, children
+//   k_stoch_walk  -- one workgroup per request: the pairs and the request's
+//                    uniforms are staged in LDS; then wavefront 0, from slot 0: children
 //                    (slots whose parent is the node, all above it) are
 //                    found in slot order by ballots over 64 slots at a time
 //                    and the i-th is accepted when u_accept * q(x) <
@@ -1144,12 +1144,13 @@ __global__ __launch_bounds__(kRowT, 1) void k_stoch_rows(StochArgs a) {
     vm_wait<0>();
 }
 
-// The walk is sequential, so one wavefront per request does it: the
-// children of a node are the slots above it whose parent it is, found in
-// slot order 64 slots at a time by a ballot, and tested in that order --
-// no block-wide scans or barriers per depth (1024 threads with three
-// barriers per depth took 10.5 us at the dedup sweep).
-constexpr int kWalkT = kWave;
+// The whole workgroup stages the request's test pairs, uniforms and parent
+// array (one load per thread: a single wavefront needed eight dependent
+// round trips at 512 slots); the walk itself is sequential, so wavefront 0
+// alone does it: the children of a node are the slots above it whose parent
+// it is, found in slot order 64 slots at a time by a ballot, and tested in
+// that order -- no block-wide scans or barriers per depth.
+constexpr int kWalkT = kT;
 __global__ __launch_bounds__(kWalkT) void k_stoch_walk(StochArgs a) {
     __shared__ int parent[kMaxSlots];
     __shared__ float2 test_sh[kMaxSlots];  // (p_i(x), q(x)) of each slot's test at its parent
@@ -1177,13 +1178,14 @@ __global__ __launch_bounds__(kWalkT) void k_stoch_walk(StochArgs a) {
     for (int i = lane; i < n; i += kWalkT) test_sh[i] = a.test[ubase + i];
     for (int i = lane; i < L * W; i += kWalkT) ua_sh[i] = a.u_acc[static_cast<size_t>(b) * L * W + i];
     build_parents<kWalkT>(a, b, n, parent);  // its barriers also publish the staging above
+    if (threadIdx.x >= kWave) return;         // no barrier follows: wavefront 0 walks
     int u = 0, d = 0;
     while (true) {
         // a node at depth L-1 is a leaf (bounds the walk on any unpacker)
         int next = -1;
         if (d + 1 < L) {
             int rank = 0;  // children of u tested so far (at most kMaxBeams, as their count is)
-            for (int c0 = u + 1; c0 < n && next < 0 && rank < kMaxBeams; c0 += kWalkT) {
+            for (int c0 = u + 1; c0 < n && next < 0 && rank < kMaxBeams; c0 += kWave) {
                 const int cs = c0 + lane;
                 uint64_t kidbits = __ballot(cs < n && parent[cs] == u);
                 while (kidbits && next < 0 && rank < kMaxBeams) {  // the same values in every lane
